@@ -1,0 +1,133 @@
+"""Seeded synthetic workloads for the decode update (inputs only, no arithmetic of the op).
+
+Both the GPU path and the CPU oracle are fed from here, so this module holds
+nothing of the method itself: it draws FP32 values with numpy, converts them to
+BF16 with torch's own converter, and builds slot-index tables.  Every array is
+host memory (numpy); BF16 tensors are carried as ``uint16`` bit patterns.
+
+Shapes follow the decode setting of the cuDNN FE-OSS page "Causal Conv1d Decode
+Update" (section "Python API" uses N=8, D=2048, W=4, L=4, SiLU; the section
+"Semantic tensor contract" fixes dtypes and strides).  No public dataset is
+involved; the pages measure none for this op.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+# A BF16 quiet-NaN bit pattern written into x's row padding (columns D..ld-1).
+# The op must never read those columns, so a NaN there can only surface in an
+# output if it did.
+PAD_SENTINEL = 0x7FC1
+# BF16 bit pattern used to pre-fill outputs and guard bands (a NaN, never produced
+# by a correct update from finite inputs).
+FILL_SENTINEL = 0x7FA5
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    name: str
+    N: int
+    D: int
+    W: int
+    L: int
+    S: int
+    ld: int
+    bias: bool
+    act: Optional[str]            # None/"identity" or "silu"
+    routing: str                  # "none" (row n -> slot n), "padded" or "unique"
+    n_unique: int = 0             # for "padded": how many real slots
+    T: int = 1                    # successive decode steps (x drawn as [T, N, D])
+    weight_dist: str = "normal"   # "normal" N(0,1) or "uniform" U(-0.5, 0.5)
+    seed: int = 0
+    layout: str = "compact"       # conv_state layout: "compact" [S, D, L] or "channel_last" [S, L, D]
+
+
+# The five synthetic configurations.  Index 0 is the tiny case, 3 is the large
+# decode batch the benchmark times.
+CONFIGS = [
+    Spec("tiny", N=4, D=64, W=4, L=3, S=4, ld=64, bias=False, act=None,
+         routing="none", seed=1),
+    Spec("page_shaped", N=8, D=2048, W=4, L=4, S=8, ld=2048, bias=True, act="silu",
+         routing="none", seed=2),
+    Spec("routed", N=64, D=4096, W=4, L=3, S=512, ld=4096, bias=True, act="silu",
+         routing="padded", n_unique=56, seed=3),
+    Spec("large_decode", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
+         routing="none", weight_dist="uniform", seed=4),
+    Spec("long_history", N=128, D=4096, W=4, L=8, S=1024, ld=4096, bias=True, act=None,
+         routing="unique", T=16, seed=5),
+]
+BY_NAME = {c.name: c for c in CONFIGS}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """FP32 -> BF16 bit patterns using torch's converter (input preparation only)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns -> FP32 using torch's converter (for reporting)."""
+    t = torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).float().numpy()
+
+
+def _normal(rng, shape, scale=1.0):
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+
+def make(spec: Spec, seed: Optional[int] = None) -> dict:
+    """Draw one workload.  Order of draws: x, weight, conv_state, bias, indices.
+
+    Returns a dict of host arrays:
+      x        uint16 [T, N, ld] (T == 1 for one step); pad columns hold PAD_SENTINEL
+      weight   uint16 [D, W]
+      state    uint16 [S, D, L] (compact) or [S, L, D] (channel_last physical)
+      bias     uint16 [D] or None
+      indices  int32 [N] or None
+    """
+    rng = np.random.default_rng(spec.seed if seed is None else seed)
+    T, N, D, W, L, S, ld = spec.T, spec.N, spec.D, spec.W, spec.L, spec.S, spec.ld
+    x = np.full((T, N, ld), PAD_SENTINEL, dtype=np.uint16)
+    x[:, :, :D] = f32_to_bf16_bits(_normal(rng, (T, N, D)))
+    if spec.weight_dist == "uniform":
+        wf = rng.uniform(-0.5, 0.5, size=(D, W)).astype(np.float32)
+    else:
+        wf = _normal(rng, (D, W))
+    weight = f32_to_bf16_bits(wf)
+    if spec.layout == "channel_last":
+        state = f32_to_bf16_bits(_normal(rng, (S, L, D)))
+    else:
+        state = f32_to_bf16_bits(_normal(rng, (S, D, L)))
+    bias = f32_to_bf16_bits(_normal(rng, (D,), 0.1)) if spec.bias else None
+    if spec.routing == "none":
+        indices = None
+    elif spec.routing == "padded":
+        real = rng.choice(S, spec.n_unique, replace=False).astype(np.int32)
+        table = np.concatenate([real, np.full(N - spec.n_unique, -1, dtype=np.int32)])
+        indices = table[rng.permutation(N)].astype(np.int32)
+    elif spec.routing == "unique":
+        indices = rng.choice(S, N, replace=False).astype(np.int32)
+    else:
+        raise ValueError(spec.routing)
+    return {"x": x, "weight": weight, "state": state, "bias": bias, "indices": indices}
+
+
+def state_strides(spec: Spec):
+    """Element strides (slot, channel, position) of the logical [S, D, L] state."""
+    if spec.layout == "channel_last":
+        return (spec.L * spec.D, 1, spec.D)
+    return (spec.D * spec.L, spec.L, 1)
+
+
+def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bool,
+                      indices: bool) -> int:
+    """Bytes one decode call must move at minimum: x and the selected state read,
+    the state written back (the history shifts, so all L values are rewritten),
+    weight, bias, output, index table.  Padding rows read no x and no state."""
+    A = active_rows
+    return (2 * A * D + 2 * A * D * L + 2 * A * D * L + 2 * D * W
+            + (2 * D if bias else 0) + 2 * N * D + (4 * N if indices else 0))

@@ -1,0 +1,190 @@
+/*
+ * Oracle for the depthwise causal conv1d decode update -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU definition of what the GPU library
+ * computes, used to check it.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load or call this file; the product path
+ * never does.  It shares no source, header, helper or table with the HIP library.
+ *
+ * Source of the semantics: the cuDNN FE-OSS page "Causal Conv1d Decode Update"
+ * (docs.nvidia.com/cudnn/latest/fe-oss-apis/causal_conv1d_update), sections
+ * "Causal Conv1d Decode Update" (the update rule, bias default, activations,
+ * slot routing and padding rows) and "Semantic tensor contract" (shapes, strides).
+ *
+ * Arithmetic: FP32, one rounding to BF16 at the end, as the accuracy contract of
+ * this library fixes ("FP32-accumulated oracle rounded once").  The page itself
+ * does not state an accumulation precision.
+ *
+ * Pins: every function here is checked against things other than itself in the
+ * CPU test suite (float64 library convolution, one-hot taps, closed forms,
+ * library BF16 conversion, hand-worked examples); no function is parity-unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EARGS 1   /* malformed arguments (shape, null pointer, L < W-1) */
+#define ORACLE_EINDEX 2  /* a slot index below -1 or not below S              */
+#define ORACLE_EDUP 3    /* two non-padding rows select the same slot         */
+
+#define ORACLE_ACT_IDENTITY 0
+#define ORACLE_ACT_SILU 1
+
+/* ---- BF16 <-> FP32 bit conversion (own code, IEEE binary32 / bfloat16) ---- */
+
+/* A BF16 value is the upper 16 bits of the FP32 with the same value: exact. */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* FP32 -> BF16, round to nearest, ties to even, on the bit pattern: add half an
+ * output ulp minus one, plus the would-be result's lowest bit, then truncate.
+ * Overflow past the largest finite BF16 carries into the exponent and yields
+ * infinity, as IEEE rounding does.  NaN stays NaN (quiet bit forced).        */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep_lsb = (u >> 16) & 1u;
+    u += 0x7fffu + keep_lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* ---- helpers of the oracle itself ---- */
+
+static float act_apply(float acc, int activation)
+{
+    if (activation == ORACLE_ACT_SILU)
+        return acc / (1.0f + expf(-acc)); /* SiLU(v) = v / (1 + exp(-v)) */
+    return acc;
+}
+
+/* Resolve and validate the slot of every row before anything is mutated.
+ * Row n uses slot n when no table is given, else table[n]; -1 is padding.
+ * Other slots must satisfy 0 <= s < S and be unique in the batch.            */
+static int resolve_slots(const int32_t *indices, int64_t n_rows, int64_t s_slots,
+                         int64_t *slot_of_row)
+{
+    for (int64_t n = 0; n < n_rows; ++n) {
+        int64_t s = indices ? (int64_t)indices[n] : n;
+        if (s < -1 || s >= s_slots)
+            return ORACLE_EINDEX;
+        slot_of_row[n] = s;
+    }
+    if (s_slots > 0) {
+        unsigned char *seen = (unsigned char *)calloc((size_t)s_slots, 1);
+        if (!seen)
+            return ORACLE_EARGS;
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t s = slot_of_row[n];
+            if (s < 0)
+                continue;
+            if (seen[s]) {
+                free(seen);
+                return ORACLE_EDUP;
+            }
+            seen[s] = 1;
+        }
+        free(seen);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * One decode step ("Causal Conv1d Decode Update" page, section of the same name).
+ *
+ *   x        BF16 bits [n_rows, d], element (n, c) at x[n*ld + c]
+ *   state    BF16 bits [s_slots, d, l], element (s, c, k) at
+ *            state[s*st_s + c*st_d + k*st_l]; k = 0 is the oldest value,
+ *            k = l-1 the newest.  Updated in place.
+ *   weight   BF16 bits [d, w] contiguous
+ *   bias     BF16 bits [d] or NULL (zero bias)
+ *   indices  int32 [n_rows] or NULL (row n -> slot n); -1 = padding row
+ *   out      BF16 bits [n_rows, d] contiguous
+ *   out_f32  optional FP32 [n_rows, d]: the value before the one BF16 rounding
+ *
+ * For a row with slot s and channel c the history is the slot's l values
+ * followed by x[n, c] (length l+1).  The state keeps the newest l of them, and
+ * the output is act(sum_j history[l+1-w+j] * weight[c, j] + bias[c]), the sum
+ * taken in FP32 with j ascending from zero and the bias added last.
+ * A padding row writes a zero output and leaves every slot untouched.
+ * Returns ORACLE_OK, or an error code before mutating anything.
+ */
+int oracle_update(const uint16_t *x, int64_t n_rows, int64_t d, int64_t ld,
+                  uint16_t *state, int64_t s_slots, int64_t l,
+                  int64_t st_s, int64_t st_d, int64_t st_l,
+                  const uint16_t *weight, int64_t w, const uint16_t *bias,
+                  const int32_t *indices, int activation,
+                  uint16_t *out, float *out_f32)
+{
+    if (n_rows < 0 || d < 1 || s_slots < 0 || w < 1 || l < w - 1 || l < 1 || ld < d)
+        return ORACLE_EARGS;
+    if (activation != ORACLE_ACT_IDENTITY && activation != ORACLE_ACT_SILU)
+        return ORACLE_EARGS;
+    if (n_rows == 0)
+        return ORACLE_OK;
+    if (!x || !state || !weight || !out)
+        return ORACLE_EARGS;
+    if (!indices && s_slots < n_rows)
+        return ORACLE_EARGS;
+
+    int64_t *slot_of_row = (int64_t *)malloc((size_t)n_rows * sizeof(int64_t));
+    float *hist = (float *)malloc((size_t)(l + 1) * sizeof(float));
+    uint16_t *hist_bits = (uint16_t *)malloc((size_t)(l + 1) * sizeof(uint16_t));
+    if (!slot_of_row || !hist || !hist_bits) {
+        free(slot_of_row); free(hist); free(hist_bits);
+        return ORACLE_EARGS;
+    }
+    int rc = resolve_slots(indices, n_rows, s_slots, slot_of_row);
+    if (rc != ORACLE_OK) {
+        free(slot_of_row); free(hist); free(hist_bits);
+        return rc;
+    }
+
+    for (int64_t n = 0; n < n_rows; ++n) {
+        int64_t s = slot_of_row[n];
+        if (s == -1) {                       /* padding row: zero output, no mutation */
+            for (int64_t c = 0; c < d; ++c) {
+                out[n * d + c] = 0;
+                if (out_f32)
+                    out_f32[n * d + c] = 0.0f;
+            }
+            continue;
+        }
+        for (int64_t c = 0; c < d; ++c) {
+            uint16_t *slot = state + s * st_s + c * st_d;
+            /* history = concat(conv_state[s, c, :], x[n, c]) */
+            for (int64_t k = 0; k < l; ++k)
+                hist_bits[k] = slot[k * st_l];
+            hist_bits[l] = x[n * ld + c];
+            /* conv_state[s, c, :] = history[-l:]  (a copy of bit patterns) */
+            for (int64_t k = 0; k < l; ++k)
+                slot[k * st_l] = hist_bits[k + 1];
+            for (int64_t k = 0; k <= l; ++k)
+                hist[k] = oracle_bf16_to_f32(hist_bits[k]);
+            /* acc = sum_j history[-w + j] * weight[c, j] + bias[c] */
+            float acc = 0.0f;
+            for (int64_t j = 0; j < w; ++j)
+                acc = acc + hist[l + 1 - w + j] * oracle_bf16_to_f32(weight[c * w + j]);
+            if (bias)
+                acc = acc + oracle_bf16_to_f32(bias[c]);
+            float y = act_apply(acc, activation);
+            if (out_f32)
+                out_f32[n * d + c] = y;
+            out[n * d + c] = oracle_f32_to_bf16(y);
+        }
+    }
+    free(slot_of_row); free(hist); free(hist_bits);
+    return ORACLE_OK;
+}
+
+/* Library self-description, so a loader can check it has the file it expects. */
+int oracle_version(void) { return 1; }
