@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the depthwise causal conv1d decode update on one MI355X.
+
+One step is one decode-update call (slot routing, x/state/weight loads, shift and
+write-back, 4-tap dot, activation, BF16 store) over one batch of the large decode
+workload: N=256 rows, D=8192 channels, W=4, L=3, S=256 slots, x row stride 8200,
+SiLU, no bias, no index table.  Inputs are seeded synthetic BF16 data already in
+HBM.  The call runs through the library's C ABI on torch's current stream.
+
+Cold-cache timing: the working set of one call (about 21 MB) fits in the 256 MB
+Infinity Cache, so consecutive steps cycle through enough independent buffer sets
+(x, state, weight, output) to exceed it; every step then reads from HBM.
+
+The timed region is K steps captured in one HIP graph and replayed once,
+bracketed by synchronisations and timed with HIP events on the stream that
+launches the kernels.  Achieved bandwidth is the algorithmic byte count of a call
+(x + selected state read + state write + weight + bias + output + index table)
+divided by the measured time per step.
+
+Prints exactly one JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s + decode rows/s, conv1d_update N=256 D=8192 W=4"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "depthwise_causal_conv1d_amd", "csrc", "update.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since the counters were taken."""
+    safe = kernel.split("<")[0]
+    path = os.path.join(PROFILES, f"traffic_{safe}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash() or vals.get("kernel") != kernel:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    """Device buffer sets for one synthetic workload, cycled per step."""
+
+    def __init__(self, spec, rotate_bytes: float, dev):
+        import numpy as np
+        import torch
+        from depthwise_causal_conv1d_amd import workloads as wl
+
+        self.spec = spec
+        data = wl.make(spec)
+        self.host = data
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        set_bytes = (data["x"][0].nbytes + data["state"].nbytes + data["weight"].nbytes
+                     + 2 * spec.N * spec.D + (data["bias"].nbytes if data["bias"] is not None else 0))
+        self.n_sets = min(128, max(1, int(math.ceil(rotate_bytes / set_bytes))))
+        self.sets = []
+        x_all = up(data["x"])  # [T, N, ld]
+        idx = None if data["indices"] is None else torch.from_numpy(data["indices"]).to(dev)
+        for i in range(self.n_sets):
+            st = up(data["state"])
+            if spec.layout == "channel_last":
+                st = st.permute(0, 2, 1)
+            self.sets.append(dict(
+                x=x_all.clone(),
+                state=st,
+                weight=up(data["weight"]),
+                bias=None if data["bias"] is None else up(data["bias"]),
+                idx=idx,
+                out=torch.empty(spec.N, spec.D, dtype=torch.bfloat16, device=dev)))
+        self.set_bytes = set_bytes
+        active = spec.N if data["indices"] is None else int((data["indices"] >= 0).sum())
+        self.bytes_per_call = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active,
+                                                   data["bias"] is not None, data["indices"] is not None)
+
+    def step(self, i: int):
+        import depthwise_causal_conv1d_amd as dc
+
+        s = self.sets[i % self.n_sets]
+        t = (i // self.n_sets) % self.spec.T
+        dc.causal_conv1d_update_out(s["x"][t, :, :self.spec.D], s["state"], s["weight"], s["bias"],
+                                    self.spec.act, out=s["out"], conv_state_indices=s["idx"])
+
+
+def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
+    import torch
+    import depthwise_causal_conv1d_amd as dc
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    wk = Workload(spec, rotate_mb * 2 ** 20, dev)
+    for i in range(warmup):
+        wk.step(i)
+    kernel = dc.dcconv_last_kernel()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if launch == "graph":
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                wk.step(warmup + i)
+        g.replay()  # one untimed replay: graph upload
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(steps):
+            wk.step(warmup + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    res = dict(workload=spec.name, kernel=kernel, ms_per_step=ms, us_per_call=ms * 1e3,
+               wall_ms_per_step=wall * 1e3 / steps, bytes_per_call=wk.bytes_per_call,
+               gbs=wk.bytes_per_call / (ms * 1e-3) / 1e9, rows_per_s=spec.N / (ms * 1e-3),
+               buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
+    res["frac"] = res["gbs"] / PEAK_HBM_GBS
+    host = wk.host
+    del wk
+    torch.cuda.empty_cache()
+    return res, host
+
+
+def cpu_baseline(spec, host, seconds: float):
+    """The oracle as it stands (single thread, plain C) on the same workload."""
+    import numpy as np
+    import oracle
+    from depthwise_causal_conv1d_amd import workloads as wl
+
+    x = np.ascontiguousarray(host["x"][0])
+    reps, t_total = 0, 0.0
+    while reps < 2 or t_total < seconds:
+        st = host["state"].copy()
+        t0 = time.perf_counter()
+        oracle.update(x, st, host["weight"], host["bias"], spec.act,
+                      conv_state_indices=host["indices"], d=spec.D, ld=spec.ld)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    active = spec.N if host["indices"] is None else int((host["indices"] >= 0).sum())
+    b = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active, host["bias"] is not None,
+                             host["indices"] is not None)
+    per_call = t_total / reps
+    return {"value": b / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}) on host "
+                      f"arrays, single thread, {per_call * 1e3:.1f} ms per call",
+            "rows_per_s": spec.N / per_call}
+
+
+def environment():
+    import torch
+    env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        props = torch.cuda.get_device_properties(0)
+        env["arch"] = getattr(props, "gcnArchName", "")
+        env["cus"] = props.multi_processor_count
+    except Exception:
+        pass
+    try:
+        cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")]
+        env["host_cpu"] = cpu[0] if cpu else ""
+        env["host_cores_visible"] = len(os.sched_getaffinity(0))
+    except Exception:
+        pass
+    return env
+
+
+def copy_calibration(mb: float):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = int(mb * 2 ** 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes 5 times")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="large_decode")
+    ap.add_argument("--rotate-mb", type=float, default=1024.0,
+                    help="total size of the buffer sets cycled through (beats the 256 MB Infinity Cache)")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the decode "
+              "update needs no communication and this build runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import depthwise_causal_conv1d_amd as dc
+    from depthwise_causal_conv1d_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dc._load()
+    if args.copy_calibration_mb > 0:
+        copy_calibration(args.copy_calibration_mb)
+        return
+
+    spec = wl.BY_NAME[args.workload]
+    res, host = measure(spec, args.steps, args.warmup, args.rotate_mb, args.launch)
+    log(f"[bench] {spec.name}: {res['us_per_call']:.3f} us/call, {res['gbs']:.1f} GB/s "
+        f"({100 * res['frac']:.1f}% of 8 TB/s), {res['rows_per_s'] / 1e6:.2f} M rows/s, kernel {res['kernel']}, "
+        f"{res['buffer_sets']} buffer sets, wall {res['wall_ms_per_step'] * 1e3:.3f} us/step")
+    others = []
+    if not args.no_other_workloads:
+        for other in wl.CONFIGS:
+            if other.name == spec.name:
+                continue
+            r, _ = measure(other, max(200, args.steps // 5), 20, min(args.rotate_mb, 512.0), args.launch)
+            log(f"[bench] {other.name}: {r['us_per_call']:.3f} us/call, {r['gbs']:.1f} GB/s, "
+                f"{r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}")
+            others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
+                           if k in ("workload", "kernel", "us_per_call", "gbs", "frac", "rows_per_s",
+                                    "bytes_per_call")})
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, host, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+
+    traffic = read_traffic(res["kernel"], spec.name)
+    line = {
+        "metric": METRIC,
+        "value": round(res["gbs"], 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "N": spec.N, "D": spec.D, "W": spec.W, "L": spec.L, "S": spec.S,
+                   "ld": spec.ld, "activation": spec.act or "identity", "bias": spec.bias,
+                   "indices": spec.routing != "none", "accumulate": "f32",
+                   "buffer_sets": res["buffer_sets"], "launch": "hipgraph" if args.launch == "graph" else "eager"},
+        "rows_per_s": res["rows_per_s"],
+        "us_per_call": res["us_per_call"],
+        "bytes_per_call": res["bytes_per_call"],
+        "kernel": res["kernel"],
+        "roofline": {"bound": "hbm", "achieved": round(res["gbs"], 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(res["frac"], 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+        "env": environment(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

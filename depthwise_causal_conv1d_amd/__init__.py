@@ -1,0 +1,200 @@
+"""MI355X-native depthwise causal conv1d decode update.
+
+Python binding over the C ABI of ``libdcconv.so`` (declared in ``include/dcconv.h``).
+It only marshals arguments: every step of the update runs in the library's gfx950
+HIP kernels.  PyTorch supplies device memory and the current stream.
+
+``dcconv_update`` mirrors the C entry point (raw device pointers as ints).
+``causal_conv1d_update`` mirrors the Python signature on the cuDNN FE-OSS page
+"Causal Conv1d Decode Update" (section "Python API"): positional ``x, conv_state,
+weight, bias, activation``, keyword-only ``cache_seqlens`` and
+``conv_state_indices``; ``conv_state`` is updated in place and a newly allocated
+output is returned.  ``causal_conv1d_update_out`` writes into a caller buffer and
+allocates nothing.
+
+There is no fallback: if the HIP library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "DCCONV_OK", "DCCONV_EINVAL", "DCCONV_EUNSUPPORTED", "DCCONV_EHIP",
+    "DCCONV_ACT_IDENTITY", "DCCONV_ACT_SILU", "DCCONV_DEV_BAD_INDEX", "DCCONV_DEV_DUP_INDEX",
+    "dcconv_abi_version", "dcconv_last_error", "dcconv_last_kernel", "dcconv_update",
+    "causal_conv1d_update", "causal_conv1d_update_out", "library_path", "DcconvError",
+]
+
+DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED, DCCONV_EHIP = 0, 1, 2, 3
+DCCONV_ACT_IDENTITY, DCCONV_ACT_SILU = 0, 1
+DCCONV_DEV_BAD_INDEX, DCCONV_DEV_DUP_INDEX = 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdcconv.so")
+_lock = threading.Lock()
+_lib = None
+
+_ACTIVATIONS = {None: DCCONV_ACT_IDENTITY, "identity": DCCONV_ACT_IDENTITY,
+                "silu": DCCONV_ACT_SILU, "swish": DCCONV_ACT_SILU}
+
+
+class DcconvError(RuntimeError):
+    """The HIP runtime refused a launch (DCCONV_EHIP)."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError(
+                    f"{_LIB_PATH} is not built; run `python -m depthwise_causal_conv1d_amd._build` "
+                    "(there is no fallback implementation)")
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64, vp, i32, cp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
+            lib.dcconv_abi_version.restype = i32
+            lib.dcconv_abi_version.argtypes = []
+            lib.dcconv_last_error.restype = cp
+            lib.dcconv_last_error.argtypes = []
+            lib.dcconv_last_kernel.restype = cp
+            lib.dcconv_last_kernel.argtypes = []
+            lib.dcconv_update.restype = i32
+            lib.dcconv_update.argtypes = [vp, i64, i64, i64,        # x, n, d, ld_x
+                                          vp, i64, i64,             # conv_state, s, l
+                                          i64, i64, i64,            # st_s, st_d, st_l
+                                          vp, i64, vp,              # weight, w, bias
+                                          vp, vp, i32,              # indices, cache_seqlens, activation
+                                          vp, vp, vp]               # out, dev_status, stream
+            _lib = lib
+    return _lib
+
+
+def _raise_for(rc: int) -> None:
+    if rc == DCCONV_OK:
+        return
+    msg = dcconv_last_error()
+    if rc == DCCONV_EINVAL:
+        raise ValueError(msg)
+    if rc == DCCONV_EUNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise DcconvError(msg or f"dcconv error {rc}")
+
+
+# ----------------------------------------------------------------- raw C ABI
+
+
+def dcconv_abi_version() -> int:
+    return _load().dcconv_abi_version()
+
+
+def dcconv_last_error() -> str:
+    return _load().dcconv_last_error().decode()
+
+
+def dcconv_last_kernel() -> str:
+    return _load().dcconv_last_kernel().decode()
+
+
+def dcconv_update(x, n, d, ld_x, conv_state, s, l, st_s, st_d, st_l, weight, w, bias,
+                  conv_state_indices, cache_seqlens, activation, out, dev_status, stream) -> int:
+    """The C entry point, one to one: pointers are ints (0/None = NULL).  Returns the
+    status code; see ``include/dcconv.h`` for the meaning of every argument."""
+    return _load().dcconv_update(x, n, d, ld_x, conv_state, s, l, st_s, st_d, st_l, weight, w,
+                                 bias, conv_state_indices, cache_seqlens, activation, out,
+                                 dev_status, stream)
+
+
+# ------------------------------------------------------------ tensor front end
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation):
+    import torch
+
+    if cache_seqlens is not None:
+        raise NotImplementedError("cache_seqlens is reserved and must be None "
+                                  "(circular-buffer state is not served)")
+    for name, t in (("x", x), ("conv_state", conv_state), ("weight", weight), ("bias", bias),
+                    ("conv_state_indices", conv_state_indices)):
+        if t is not None and t.requires_grad:
+            raise NotImplementedError(f"inference only: {name} requires grad (training is not served)")
+    if x.dim() == 3:
+        raise NotImplementedError("a 3-D x (multi-token update) is not served by this call")
+    if x.dim() != 2:
+        raise ValueError(f"x must be [N, D], got shape {tuple(x.shape)}")
+    if conv_state.dim() != 3:
+        raise ValueError(f"conv_state must be [S, D, L], got shape {tuple(conv_state.shape)}")
+    if weight.dim() != 2:
+        raise ValueError(f"weight must be [D, W], got shape {tuple(weight.shape)}")
+    for name, t in (("x", x), ("conv_state", conv_state), ("weight", weight), ("bias", bias)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if conv_state_indices is not None and conv_state_indices.dtype != torch.int32:
+        raise ValueError(f"conv_state_indices must be int32, got {conv_state_indices.dtype}")
+    if activation not in _ACTIVATIONS:
+        raise ValueError(f"activation must be None, 'identity', 'silu' or 'swish', got {activation!r}")
+    N, D = x.shape
+    if conv_state.shape[1] != D or weight.shape[0] != D:
+        raise ValueError(f"channel counts differ: x {D}, conv_state {conv_state.shape[1]}, weight {weight.shape[0]}")
+    if x.stride(1) != 1 and D > 1:
+        raise ValueError("x must have unit stride along channels (strides (ld, 1))")
+    if not weight.is_contiguous():
+        raise ValueError("weight must be contiguous [D, W]")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != D or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [D] tensor")
+    if conv_state_indices is not None and (conv_state_indices.dim() != 1 or conv_state_indices.shape[0] != N
+                                           or not conv_state_indices.is_contiguous()):
+        raise ValueError("conv_state_indices must be a contiguous int32 [N] tensor")
+    dev = x.device
+    for name, t in (("conv_state", conv_state), ("weight", weight), ("bias", bias),
+                    ("conv_state_indices", conv_state_indices)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, x on {dev}")
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+
+
+def causal_conv1d_update_out(x, conv_state, weight, bias=None, activation=None, *, out,
+                             cache_seqlens=None, conv_state_indices=None, dev_status=None):
+    """Like ``causal_conv1d_update`` but writes ``out`` (bf16 [N, D], contiguous) and
+    allocates nothing.  ``dev_status`` (int32 [1] on the device, optional) receives
+    DCCONV_DEV_* bits for rejected routing entries."""
+    import torch
+
+    _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation)
+    N, D = x.shape
+    if out.shape != (N, D) or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous bfloat16 [N, D] tensor on x's device")
+    if dev_status is not None and (dev_status.dtype != torch.int32 or dev_status.device != x.device):
+        raise ValueError("dev_status must be an int32 tensor on x's device")
+    S, _, L = conv_state.shape
+    st = conv_state.stride()
+    ld = x.stride(0) if N > 1 else D
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = dcconv_update(_ptr(x), N, D, ld, _ptr(conv_state), S, L, st[0], st[1], st[2],
+                           _ptr(weight), weight.shape[1], _ptr(bias), _ptr(conv_state_indices), None,
+                           _ACTIVATIONS[activation], _ptr(out), _ptr(dev_status), stream)
+    _raise_for(rc)
+    return out
+
+
+def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None, *,
+                         cache_seqlens=None, conv_state_indices=None):
+    """One decode step: updates ``conv_state`` in place and returns a new bf16 [N, D]
+    output (page "Causal Conv1d Decode Update", section "Python API")."""
+    import torch
+
+    _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation)
+    out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    return causal_conv1d_update_out(x, conv_state, weight, bias, activation, out=out,
+                                    conv_state_indices=conv_state_indices)

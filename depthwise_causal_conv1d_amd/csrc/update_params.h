@@ -1,0 +1,31 @@
+// Internal interface between the C-ABI front end (abi.hip) and the update
+// kernels (update.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dcconv {
+
+// Everything one decode-update launch needs, already validated on the host.
+struct UpdateParams {
+    const uint16_t *x;      // BF16 [n, d], row stride ld (elements)
+    uint16_t *state;        // BF16 logical [s, d, l] at strides (st_s, st_d, st_l)
+    const uint16_t *weight; // BF16 [d, 4]
+    const uint16_t *bias;   // BF16 [d] or nullptr
+    const int32_t *idx;     // int32 [n] or nullptr
+    int32_t *status;        // device int32 or nullptr
+    uint16_t *out;          // BF16 [n, d]
+    int64_t ld;
+    int64_t st_s, st_d, st_l;
+    int32_t n, d, s, l;
+};
+
+enum class StateLayout { Compact, ChannelLast };
+
+// Picks the specialisation, launches it on `stream` and stores its name in
+// *kernel_name.  Returns hipSuccess or the launch error.
+hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation,
+                         hipStream_t stream, const char **kernel_name);
+
+}  // namespace dcconv

@@ -1,0 +1,136 @@
+/*
+ * dcconv.h -- C ABI of the MI355X (gfx950) depthwise causal conv1d library.
+ *
+ * The operation is the decode update described on the cuDNN FE-OSS page
+ * "Causal Conv1d Decode Update" (docs.nvidia.com/cudnn/latest/fe-oss-apis/
+ * causal_conv1d_update): for every decode row n, channel d and the cache slot s
+ * the row selects,
+ *
+ *     history            = concat(conv_state[s, d, :], x[n, d])      (length L+1)
+ *     conv_state[s, d, :] = newest L values of history
+ *     out[n, d]          = act(sum_j history[L+1-W+j] * weight[d, j] + bias[d])
+ *
+ * (page section "Causal Conv1d Decode Update").  Sums are formed in FP32 and
+ * rounded once to BF16 (round to nearest even).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP device memory or memory the
+ *    device can address), except where a comment says otherwise.
+ *  - The caller owns every buffer.  The library allocates nothing, never
+ *    synchronises, never reads device memory from the host and converts nothing,
+ *    so a call may be captured into a HIP graph (stable pointers).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *    asynchronous; results are visible after the stream is synchronised.
+ *  - Metadata is validated on the host, in full, before anything is enqueued.
+ *    A non-zero return means nothing was enqueued; dcconv_last_error() then
+ *    describes the problem (thread-local, valid until the next call on the same
+ *    thread).
+ *  - Elements are BF16 carried as 16-bit patterns; indices are int32.
+ */
+#ifndef DCCONV_H
+#define DCCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCCONV_ABI_VERSION 1
+
+/* Return codes.  The page distinguishes a contract violation (Python ValueError)
+ * from a valid request the implementation does not serve (NotImplementedError);
+ * section "Current native implementation". */
+enum {
+    DCCONV_OK = 0,
+    DCCONV_EINVAL = 1,       /* contract violation: shape, stride, alignment, overlap, null */
+    DCCONV_EUNSUPPORTED = 2, /* semantically valid but not served (e.g. W != 4, cache_seqlens) */
+    DCCONV_EHIP = 3          /* the HIP runtime refused the launch (hipGetLastError) */
+};
+
+/* Activations (page section "Causal Conv1d Decode Update": None/"identity" and
+ * "silu"/"swish").  Each is a separate compiled kernel; the identity kernel
+ * contains no activation code. */
+enum { DCCONV_ACT_IDENTITY = 0, DCCONV_ACT_SILU = 1 };
+
+/* Bits OR-ed into *dev_status by the device when a routing entry is rejected. */
+enum {
+    DCCONV_DEV_BAD_INDEX = 1, /* an index below -1, or not below S           */
+    DCCONV_DEV_DUP_INDEX = 2  /* two rows of the batch select one real slot  */
+};
+
+/* The DCCONV_ABI_VERSION the library was built with. */
+int dcconv_abi_version(void);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char *dcconv_last_error(void);
+
+/* Name of the kernel specialisation the last successful call on the calling
+ * thread enqueued ("" if that call enqueued nothing).  Lets a benchmark prove
+ * which route ran. */
+const char *dcconv_last_kernel(void);
+
+/*
+ * dcconv_update -- one decode step, in place.
+ * Defined by the page section "Causal Conv1d Decode Update" (update rule, bias
+ * default, activations, slot routing, padding rows) and section "Semantic tensor
+ * contract" (shapes, strides, alignment); the limits of the served subset follow
+ * section "Current native implementation".
+ *
+ * x           BF16 [n, d], element (r, c) at x[r*ld_x + c].  ld_x == d, or
+ *             ld_x > d with ld_x % 8 == 0 (16-byte aligned rows).  Columns
+ *             d..ld_x-1 are never read.
+ * n           decode rows, n >= 0.  n == 0 returns DCCONV_OK and enqueues nothing.
+ * d           channels, d >= 1.
+ * conv_state  BF16 [s, d, l], READ AND WRITTEN.  Element (slot, c, k) at
+ *             conv_state[slot*st_s + c*st_d + k*st_l]; k = 0 is the oldest value.
+ *             Accepted layouts: compact (st_d == l, st_l == 1, st_s >= d*l) and
+ *             channel-last (st_d == 1, st_l == d, st_s >= l*d; the layout a
+ *             full-sequence prefill hands over).
+ * s           slots, s >= 0; without an index table s >= n (row r uses slot r).
+ *             With s == 0 every row must be padding and conv_state may be NULL.
+ * l           history length, l >= w - 1.
+ * weight      BF16 [d, w] contiguous.  Only w == 4 is served.
+ * bias        BF16 [d] or NULL (zero bias).
+ * conv_state_indices  int32 [n] or NULL.  Row r uses slot conv_state_indices[r];
+ *             -1 marks a padding row: its output is zero and no slot changes
+ *             (repeated -1 is allowed).  Other values must lie in [0, s) and be
+ *             unique within the call.  An entry below -1 or >= s makes that row
+ *             behave as a padding row and sets DCCONV_DEV_BAD_INDEX.  When
+ *             dev_status is non-NULL every row whose slot is shared with another
+ *             row is also treated as padding (so that slot is left untouched)
+ *             and DCCONV_DEV_DUP_INDEX is set; when dev_status is NULL duplicates
+ *             are not detected and the result for the shared slot is unspecified
+ *             (the page calls such an update "not transactional").
+ * cache_seqlens  reserved; must be NULL, otherwise DCCONV_EUNSUPPORTED
+ *             (the page raises NotImplementedError for anything but None).
+ * activation  DCCONV_ACT_IDENTITY or DCCONV_ACT_SILU (SiLU(v) = v / (1 + e^-v)).
+ * out         BF16 [n, d] contiguous, written.  Must not overlap any operand.
+ * dev_status  NULL, or a device int32 the kernel ORs DCCONV_DEV_* bits into.
+ *             It is never cleared by the library.
+ * stream      hipStream_t to enqueue on; NULL = null stream.
+ *
+ * Alignment: every BF16 pointer 16-byte aligned, indices and dev_status 4-byte
+ * aligned (page section "Current native implementation").  conv_state must not
+ * overlap x, weight, bias, the index table, out or dev_status.
+ *
+ * Returns DCCONV_OK, DCCONV_EINVAL (contract violation), DCCONV_EUNSUPPORTED
+ * (valid but not served), or DCCONV_EHIP (launch refused by the runtime).
+ */
+int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
+                  void *conv_state, int64_t s, int64_t l,
+                  int64_t st_s, int64_t st_d, int64_t st_l,
+                  const void *weight, int64_t w,
+                  const void *bias,
+                  const int32_t *conv_state_indices,
+                  const int32_t *cache_seqlens,
+                  int activation,
+                  void *out,
+                  int32_t *dev_status,
+                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCCONV_H */

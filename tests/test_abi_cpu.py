@@ -1,0 +1,204 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/dcconv.h declares, and refuses every malformed or unserved request on the
+host before anything reaches the HIP runtime.
+
+The refusals follow the cuDNN FE-OSS page "Causal Conv1d Decode Update": section
+"Semantic tensor contract" (x row-stride rule, L >= W-1) and section "Current
+native implementation" (W = 4, 16-byte alignment, cache_seqlens must be None).
+
+The raw-pointer tests pass made-up (never dereferenced) device addresses, so they
+only run where no GPU is visible; the GPU suite repeats the refusals on real
+tensors.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import depthwise_causal_conv1d_amd as dc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcconv.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="made-up pointers are only passed where no GPU exists")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcconv_\w+)\s*\(", text)))
+
+
+def _header_constants():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"\b(DCCONV_[A-Z_]+)\s*=\s*(\d+)", text))
+    consts.update(re.findall(r"#define\s+(DCCONV_[A-Z_]+)\s+(\d+)", text))
+    return {k: int(v) for k, v in consts.items()}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dc._load()
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = _declared()
+    assert {"dcconv_update", "dcconv_abi_version", "dcconv_last_error", "dcconv_last_kernel"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in dcconv.h but not exported"
+
+
+def test_abi_version_and_constants_match_header(lib):
+    c = _header_constants()
+    assert dc.dcconv_abi_version() == c["DCCONV_ABI_VERSION"]
+    for k, v in c.items():
+        if k == "DCCONV_ABI_VERSION" or k == "DCCONV_H":
+            continue
+        assert getattr(dc, k) == v, k
+
+
+def test_binding_names_match_c_names():
+    for name in _declared():
+        assert callable(getattr(dc, name)), name
+
+
+# made-up, 16-byte aligned, far apart device addresses (never dereferenced)
+X, ST, WT, BI, IX, OUT, STAT = (0x10000000 * (k + 1) for k in range(7))
+
+
+def _args(**over):
+    a = dict(x=X, n=4, d=64, ld_x=64, conv_state=ST, s=4, l=3, st_s=192, st_d=3, st_l=1,
+             weight=WT, w=4, bias=None, conv_state_indices=None, cache_seqlens=None,
+             activation=0, out=OUT, dev_status=None, stream=None)
+    a.update(over)
+    return a
+
+
+def _call(**over):
+    a = _args(**over)
+    return dc.dcconv_update(**a)
+
+
+DECLINES = [
+    # (overrides, expected code, message fragment)
+    (dict(n=-1), dc.DCCONV_EINVAL, "n (decode rows)"),
+    (dict(d=0), dc.DCCONV_EINVAL, "d (channels)"),
+    (dict(s=-1), dc.DCCONV_EINVAL, "s (state slots)"),
+    (dict(w=0), dc.DCCONV_EINVAL, "filter width"),
+    (dict(l=2, st_d=2, st_s=128), dc.DCCONV_EINVAL, "must be >= w-1"),
+    (dict(ld_x=63), dc.DCCONV_EINVAL, "smaller than d"),
+    (dict(ld_x=70), dc.DCCONV_EINVAL, "ld_x % 8 == 0"),
+    (dict(activation=2), dc.DCCONV_EINVAL, "activation"),
+    (dict(st_d=-3), dc.DCCONV_EINVAL, "non-negative"),
+    (dict(cache_seqlens=IX), dc.DCCONV_EUNSUPPORTED, "cache_seqlens"),
+    (dict(w=3), dc.DCCONV_EUNSUPPORTED, "w=4"),
+    (dict(w=5, l=4, st_d=4, st_s=256), dc.DCCONV_EUNSUPPORTED, "w=4"),
+    (dict(st_s=192, st_d=1, st_l=2), dc.DCCONV_EUNSUPPORTED, "neither compact"),
+    (dict(st_s=100), dc.DCCONV_EUNSUPPORTED, "neither compact"),
+    (dict(x=None), dc.DCCONV_EINVAL, "non-NULL"),
+    (dict(conv_state=None), dc.DCCONV_EINVAL, "non-NULL"),
+    (dict(weight=None), dc.DCCONV_EINVAL, "non-NULL"),
+    (dict(out=None), dc.DCCONV_EINVAL, "non-NULL"),
+    (dict(s=3), dc.DCCONV_EINVAL, "must be >= n"),
+    (dict(x=X + 2), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(conv_state=ST + 8), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(weight=WT + 4), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(out=OUT + 2), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(bias=BI + 2), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(conv_state_indices=IX + 2), dc.DCCONV_EINVAL, "4-byte aligned"),
+    (dict(dev_status=STAT + 1), dc.DCCONV_EINVAL, "4-byte aligned"),
+    (dict(out=X + 256), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(out=X), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(conv_state=X + 128), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(out=WT + 64), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(conv_state_indices=ST + 16), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(dev_status=OUT + 8), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(bias=ST + 64), dc.DCCONV_EINVAL, "overlaps"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code,frag", DECLINES, ids=[str(d[0]) for d in DECLINES])
+def test_host_refusals(over, code, frag):
+    rc = _call(**over)
+    assert rc == code, (rc, dc.dcconv_last_error())
+    assert frag in dc.dcconv_last_error()
+    assert dc.dcconv_last_kernel() == ""
+
+
+@no_gpu
+def test_zero_rows_enqueue_nothing():
+    assert _call(n=0, x=None, out=None, conv_state=None, weight=None) == dc.DCCONV_OK
+    assert dc.dcconv_last_error() == "" and dc.dcconv_last_kernel() == ""
+
+
+@no_gpu
+def test_zero_rows_still_checks_metadata():
+    assert _call(n=0, w=3) == dc.DCCONV_EUNSUPPORTED
+    assert _call(n=0, l=2, st_d=2, st_s=128) == dc.DCCONV_EINVAL
+
+
+@no_gpu
+def test_error_message_is_thread_local():
+    import threading
+    assert _call(d=0) == dc.DCCONV_EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = dc.dcconv_last_error()
+
+    t = threading.Thread(target=other)
+    t.start(); t.join()
+    assert seen["msg"] == ""
+    assert "d (channels)" in dc.dcconv_last_error()
+
+
+# ----------------------------------------------------- tensor front-end refusals
+
+
+def _cpu_args(N=4, D=16, L=3, S=4):
+    bf = torch.bfloat16
+    return (torch.zeros(N, D, dtype=bf), torch.zeros(S, D, L, dtype=bf), torch.zeros(D, 4, dtype=bf))
+
+
+def test_frontend_refuses_cache_seqlens():
+    x, st, w = _cpu_args()
+    with pytest.raises(NotImplementedError, match="cache_seqlens"):
+        dc.causal_conv1d_update(x, st, w, cache_seqlens=torch.zeros(4, dtype=torch.int32))
+
+
+def test_frontend_refuses_multi_token_x():
+    _, st, w = _cpu_args()
+    with pytest.raises(NotImplementedError, match="3-D x"):
+        dc.causal_conv1d_update(torch.zeros(4, 16, 2, dtype=torch.bfloat16), st, w)
+
+
+def test_frontend_refuses_autograd_inputs():
+    x, st, w = _cpu_args()
+    w = w.float().requires_grad_(True)
+    with pytest.raises(NotImplementedError, match="inference only"):
+        dc.causal_conv1d_update(x, st, w)
+
+
+@pytest.mark.parametrize("bad", ["dtype_x", "dtype_idx", "act", "shape", "channels", "stride", "device"])
+def test_frontend_contract_violations(bad):
+    x, st, w = _cpu_args()
+    kw = {}
+    act = "silu"
+    if bad == "dtype_x":
+        x = x.float()
+    elif bad == "dtype_idx":
+        kw["conv_state_indices"] = torch.zeros(4, dtype=torch.int64)
+    elif bad == "act":
+        act = "gelu"
+    elif bad == "shape":
+        x = torch.zeros(4, dtype=torch.bfloat16)
+    elif bad == "channels":
+        w = torch.zeros(8, 4, dtype=torch.bfloat16)
+    elif bad == "stride":
+        x = torch.zeros(16, 4, dtype=torch.bfloat16).t()
+    with pytest.raises(ValueError):
+        dc.causal_conv1d_update(x, st, w, None, act, **kw)
