@@ -6,29 +6,34 @@
 // act(sum_j history[L+1-W+j] * weight[c, j] + bias[c]) with W = 4.
 //
 // The update is a pure stream: every byte of x, of the selected state and of the
-// output is touched exactly once, weight and bias are re-read from L2 by every
-// row.  It is bound by HBM bandwidth, so the kernels are organised around
-// coalesced 16-byte accesses, not around arithmetic (there is no contraction, so
-// no MFMA).
+// output is touched exactly once; weight and bias are re-read from L2 by every
+// row group.  It is bound by HBM bandwidth, so the kernels are organised around
+// coalesced 16-byte accesses and around keeping many of them in flight, not
+// around arithmetic (there is no contraction, so no MFMA).
 //
-//  * update_compact_v8<L, ACT>: the fast path for the compact [S, D, L] layout.
-//    One wavefront owns one (row, 512-channel tile); each lane owns 8 adjacent
+//  * update_compact_v8<L, ACT, R>: the fast path for the compact [S, D, L] layout.
+//    One wavefront owns R rows of one 512-channel tile; each lane owns 8 adjacent
 //    channels, so x, weight, bias and out move as one 16-byte vector per lane.
-//    The tile's state is a contiguous 1 KiB * L run.  It is loaded with L fully
-//    coalesced 16-byte loads per lane into a per-wave LDS buffer, read back in
-//    per-lane channel order, shifted in registers, written back to LDS and
-//    stored with L coalesced 16-byte stores.  Waves never share LDS, so the only
-//    synchronisation is wave-local.
+//    A row's tile of state is a contiguous 1 KiB * L run.  The wave issues every
+//    load of its R rows up front (weights and bias once for all R rows), then
+//    finishes the rows in order, each as soon as its own loads have landed: the
+//    state run goes through a per-wave LDS stage (written in coalesced order,
+//    read back in per-lane channel order), is shifted in registers with byte
+//    permutes, goes back through the stage and leaves with L coalesced 16-byte
+//    stores.  Waves never share LDS, so all synchronisation is wave-local.
+//    The single-use streams (x, state, out) carry the non-temporal hint, which
+//    keeps them from displacing the reused weights and routing table in the
+//    caches.
 //  * update_channel_last_v8<ACT>: the [S, L, D] layout a prefill hands over.
-//    Every history position is a contiguous plane over channels, so the lane
-//    that owns 8 channels loads and stores each plane with one coalesced 16-byte
+//    Every history position is a contiguous plane over channels, so the lane that
+//    owns 8 channels loads and stores each plane with one coalesced 16-byte
 //    access and the shift is a plane renaming; no LDS is needed.
 //  * update_scalar<ACT>: one thread per (row, channel), any stride, any L >= 3,
 //    any D.  Serves what the vector paths do not (D or row stride not a multiple
 //    of 8, L > 8).
 //
-// Routing is resolved per wavefront: the slot index is wave-uniform, so a padding
-// or rejected row is one uniform branch that writes zeros and touches no state.
+// Routing is resolved per row and is wave-uniform, so a padding or rejected row
+// is one uniform branch that writes zeros and touches no state.
 #include <stdint.h>
 
 #include "dcconv.h"
@@ -40,17 +45,51 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kChPerLane = 8;                   // one 16-byte BF16 vector
 constexpr int kChPerWave = kWave * kChPerLane;  // 512 channels
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 2;
 constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kScalarTile = kBlock;             // channels per block in the scalar path
+constexpr int kScalarBlock = 256;               // channels per block in the scalar path
 constexpr int64_t kMaxBlocks = 1 << 20;         // grid cap; the kernels stride over units
+// Two rows per wave once the grid still has this many waves: fewer, fuller waves
+// keep more bytes in flight per wave and share one weight load between rows.
+constexpr int64_t kMinWavesForTwoRows = 1024;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
-    return __uint_as_float(bits16 << 16);
+// Single-use streams: non-temporal 16-byte accesses.
+__device__ __forceinline__ u32x4 load_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
+__device__ __forceinline__ void store_stream(void *p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+// Reused data (weights, bias): ordinary cached loads.
+__device__ __forceinline__ u32x4 load_cached(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Raw buffer accesses: a descriptor holds a base address and a byte count, and
+// the hardware turns any access at or beyond the count into a zero read or a
+// dropped write.  Word 3 is the gfx9 raw-buffer format (32-bit data format).
+typedef __amdgpu_buffer_rsrc_t Buffer;
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCached = 0;  // cache policy: default
+constexpr int kStream = 2;  // cache policy: non-temporal
+__device__ __forceinline__ Buffer make_buffer(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+template <int POLICY>
+__device__ __forceinline__ u32x4 buffer_load(Buffer b, uint32_t offset) {
+    return __builtin_amdgcn_raw_buffer_load_b128(b, offset, 0, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ void buffer_store(u32x4 v, Buffer b, uint32_t offset) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b, offset, 0, POLICY);
+}
+
+// BF16 held in the low / high half of a 32-bit word, as FP32 (exact).
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // Two FP32 values -> one word holding two BF16 (round to nearest even; gfx950
 // converts a pair in one instruction).
@@ -69,9 +108,13 @@ template <>
 __device__ __forceinline__ float activate<DCCONV_ACT_IDENTITY>(float a) {
     return a;
 }
+// SiLU(a) = a / (1 + e^-a), with the hardware base-2 exponential and reciprocal
+// (each within about one FP32 ulp; the result is far inside one BF16 ulp).
+// a -> -inf gives a * rcp(inf) = -0, a -> +inf gives a.
 template <>
 __device__ __forceinline__ float activate<DCCONV_ACT_SILU>(float a) {
-    return a / (1.0f + __expf(-a));  // SiLU(a) = a / (1 + e^-a)
+    constexpr float kMinusLog2e = -1.4426950408889634f;
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * kMinusLog2e));
 }
 
 // Orders this wave's LDS accesses across lanes.  LDS instructions of one
@@ -109,130 +152,185 @@ __device__ __forceinline__ int route_row(const UpdateParams &p, int row, int lan
     return slot;
 }
 
-// 16-bit element e of a register array of packed BF16 pairs (e is a constant
-// after unrolling, so this folds to a shift or a mask).
+// 16-bit element e of an array of packed BF16 pairs, as FP32 (e is a constant
+// after unrolling, so this folds to one shift or mask).
 template <int NW>
-__device__ __forceinline__ uint32_t elem(const uint32_t (&w)[NW], int e) {
-    return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+__device__ __forceinline__ float elem_f32(const uint32_t (&w)[NW], int e) {
+    return (e & 1) ? hi_f32(w[e >> 1]) : lo_f32(w[e >> 1]);
 }
 
 // The arithmetic for the 8 channels a lane owns.
-//   hist[8*L]: the old state of the 8 channels, channel-major (oldest first)
-//   xw[4], ww[16], bw[4]: x, weight [8][4] and bias of the 8 channels
-// Produces the 8 outputs (packed) and the new state (same order as hist).
+//   hist[4L]: the old state of the 8 channels, channel-major (oldest first)
+//   xw[4]:    x of the 8 channels;  wf[32]: weights [8][4] as FP32;  bf[8]: bias
+// Produces the 8 outputs (packed BF16) and the new state (same order as hist).
 template <int L, int ACT>
 __device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uint32_t (&xw)[4],
-                                        const uint32_t (&ww)[16], const uint32_t (&bw)[4],
-                                        bool has_bias, uint32_t (&outw)[4],
-                                        uint32_t (&nhist)[4 * L]) {
+                                        const float (&wf)[32], const float (&bf)[8], bool has_bias,
+                                        uint32_t (&outw)[4], uint32_t (&nhist)[4 * L]) {
     float y[kChPerLane];
 #pragma unroll
     for (int c = 0; c < kChPerLane; ++c) {
         // history[L+1-W+j] for W = 4: the newest three state values, then x.
-        const float h0 = bf16_bits_to_f32(elem(hist, c * L + L - 3));
-        const float h1 = bf16_bits_to_f32(elem(hist, c * L + L - 2));
-        const float h2 = bf16_bits_to_f32(elem(hist, c * L + L - 1));
-        const float h3 = bf16_bits_to_f32(elem(xw, c));
         // BF16 x BF16 products are exact in FP32, so the fused multiply-adds give
         // the same bits as separate products summed from j = 0 upward.
-        float acc = h0 * bf16_bits_to_f32(elem(ww, 4 * c + 0));
-        acc = __builtin_fmaf(h1, bf16_bits_to_f32(elem(ww, 4 * c + 1)), acc);
-        acc = __builtin_fmaf(h2, bf16_bits_to_f32(elem(ww, 4 * c + 2)), acc);
-        acc = __builtin_fmaf(h3, bf16_bits_to_f32(elem(ww, 4 * c + 3)), acc);
-        if (has_bias) acc += bf16_bits_to_f32(elem(bw, c));
+        float acc = elem_f32(hist, c * L + L - 3) * wf[4 * c + 0];
+        acc = __builtin_fmaf(elem_f32(hist, c * L + L - 2), wf[4 * c + 1], acc);
+        acc = __builtin_fmaf(elem_f32(hist, c * L + L - 1), wf[4 * c + 2], acc);
+        acc = __builtin_fmaf(elem_f32(xw, c), wf[4 * c + 3], acc);
+        if (has_bias) acc += bf[c];
         y[c] = activate<ACT>(acc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) outw[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
     // New state: each channel's history moves one place towards the oldest end
-    // and x becomes the newest value.  Bit copies only.
+    // and x becomes the newest value.  New element e is x[e / L] when e is the
+    // last position of its channel, else old element e + 1.  Each new word (two
+    // elements) is one byte permute of the two words its halves come from.
 #pragma unroll
     for (int i = 0; i < 4 * L; ++i) {
-        uint32_t half[2];
+        uint32_t src[2];
+        int half[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int e = 2 * i + k;
-            half[k] = (e % L == L - 1) ? elem(xw, e / L) : elem(hist, e + 1);
+            if (e % L == L - 1) {
+                src[k] = xw[(e / L) >> 1];
+                half[k] = (e / L) & 1;
+            } else {
+                src[k] = hist[(e + 1) >> 1];
+                half[k] = (e + 1) & 1;
+            }
         }
-        nhist[i] = half[0] | (half[1] << 16);
+        // v_perm_b32(a, b, sel): selector bytes 0-3 pick bytes of b, 4-7 bytes of a.
+        const uint32_t sel_lo = half[0] ? 0x0302u : 0x0100u;  // from b = src[0]
+        const uint32_t sel_hi = half[1] ? 0x0706u : 0x0504u;  // from a = src[1]
+        nhist[i] = __builtin_amdgcn_perm(src[1], src[0], (sel_hi << 16) | sel_lo);
     }
 }
 
-__device__ __forceinline__ void unpack4(const uint4 &v, uint32_t *w) {
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-}
-
-template <int L, int ACT>
+template <int L, int ACT, int R>
 __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int tiles_per_row,
                                                             int64_t units) {
-    __shared__ uint4 stage_all[kWavesPerBlock][kWave * L];
+    __shared__ u32x4 stage_all[kWavesPerBlock][R][kWave * L];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    uint4 *stage = stage_all[wave];
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;  // this lane's 16-byte vector in a 512-channel run
 
     for (int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + wave; unit < units;
          unit += (int64_t)gridDim.x * kWavesPerBlock) {
-        const int row = (int)(unit / tiles_per_row);
-        const int c0 = (int)(unit - (int64_t)row * tiles_per_row) * kChPerWave;
+        const int group = (int)(unit / tiles_per_row);
+        const int c0 = (int)(unit - (int64_t)group * tiles_per_row) * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
-        const bool owns = lane < lanes_used;
-        uint4 *out_v = reinterpret_cast<uint4 *>(p.out + (int64_t)row * p.d + c0) + lane;
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;  // x / out / bias bytes of the tile
 
-        const int slot = route_row(p, row, lane);
-        if (slot < 0) {
-            if (owns) *out_v = make_uint4(0u, 0u, 0u, 0u);
-            continue;
-        }
-
-        // Issue every load of the unit before any use.
-        uint4 *chunks = reinterpret_cast<uint4 *>(p.state + (int64_t)slot * p.st_s + (int64_t)c0 * L);
-        const int n_chunks = lanes_used * L;
-        uint4 sv[L];
+        // Route every row of the group (wave-uniform): slot, -1 = write zeros,
+        // -2 = no such row.
+        int slot[R];
 #pragma unroll
-        for (int j = 0; j < L; ++j) {
-            const int g = j * kWave + lane;
-            sv[j] = g < n_chunks ? chunks[g] : make_uint4(0u, 0u, 0u, 0u);
+        for (int r = 0; r < R; ++r) {
+            const int row = group * R + r;
+            // route_row's result is the same in every lane; saying so keeps the
+            // buffer descriptors built from it in scalar registers.
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p, row, lane) : -2);
         }
-        uint4 xv = make_uint4(0u, 0u, 0u, 0u), bv = make_uint4(0u, 0u, 0u, 0u);
-        uint4 wv[4] = {};
+
+        // Issue every load up front: weights and bias once, then each row's x and
+        // state run.  Buffer descriptors bound each access: a row that must not
+        // touch memory gets an empty descriptor (its loads return zeros, its
+        // stores are dropped) and the lanes past a ragged tile's end fall outside
+        // the descriptor.  No load sits under a branch, so the compiler waits for
+        // each row's own data only.
         const bool has_bias = p.bias != nullptr;
-        if (owns) {
-            const int c = c0 + lane * kChPerLane;
-            xv = *reinterpret_cast<const uint4 *>(p.x + (int64_t)row * p.ld + c);
-            const uint4 *wp = reinterpret_cast<const uint4 *>(p.weight + (int64_t)c * 4);
+        const Buffer wbuf = make_buffer(p.weight + (int64_t)c0 * 4, vec_bytes * 4u);
+        const Buffer bbuf = make_buffer(has_bias ? p.bias + c0 : p.weight, has_bias ? vec_bytes : 0u);
+        u32x4 wv[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) wv[k] = wp[k];
-            if (has_bias) bv = *reinterpret_cast<const uint4 *>(p.bias + c);
+        for (int k = 0; k < 4; ++k) wv[k] = buffer_load<kCached>(wbuf, lane_bytes * 4u + 16u * k);
+        const u32x4 bv = buffer_load<kCached>(bbuf, lane_bytes);
+        Buffer sbuf[R];
+        u32x4 xv[R], sv[R][L];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool live = slot[r] >= 0;
+            const int row = min(group * R + r, p.n - 1);
+            const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u);
+            sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + (int64_t)c0 * L : p.x,
+                                  live ? vec_bytes * L : 0u);
+            xv[r] = buffer_load<kStream>(xbuf, lane_bytes);
+#pragma unroll
+            for (int j = 0; j < L; ++j) sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+        }
+        float wf[32], bf[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wf[8 * k + 2 * q] = lo_f32(wv[k][q]);
+                wf[8 * k + 2 * q + 1] = hi_f32(wv[k][q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bf[2 * q] = lo_f32(bv[q]);
+            bf[2 * q + 1] = hi_f32(bv[q]);
         }
 
-        // Coalesced chunk order -> per-lane channel order, through LDS.
+        // Finish the rows in order, each once its own loads have landed, and
+        // issue every store at the end.  On gfx9 loads and stores share one
+        // completion counter that drains in order, and a store's data registers
+        // may not be reused before it completes; so any wait placed after a store
+        // (for the next row's loads, or for a register the store still holds)
+        // would also wait for that store to be acknowledged by memory.  Keeping
+        // all stores last means no wait ever follows one.
+        if (slot[0] >= 0) {
 #pragma unroll
-        for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[j];
-        wave_lds_sync();
-        uint32_t hist[4 * L];
-#pragma unroll
-        for (int k = 0; k < L; ++k) unpack4(stage[lane * L + k], &hist[4 * k]);
-
-        uint32_t xw[4], ww[16], bw[4], outw[4], nhist[4 * L];
-        unpack4(xv, xw);
-        unpack4(bv, bw);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) unpack4(wv[k], &ww[4 * k]);
-        update8<L, ACT>(hist, xw, ww, bw, has_bias, outw, nhist);
-
-        // Per-lane channel order -> coalesced chunk order, through LDS.
-        wave_lds_sync();
-#pragma unroll
-        for (int k = 0; k < L; ++k)
-            stage[lane * L + k] = make_uint4(nhist[4 * k], nhist[4 * k + 1], nhist[4 * k + 2], nhist[4 * k + 3]);
-        wave_lds_sync();
-#pragma unroll
-        for (int j = 0; j < L; ++j) {
-            const int g = j * kWave + lane;
-            const uint4 v = stage[g];
-            if (g < n_chunks) chunks[g] = v;
+            for (int j = 0; j < L; ++j) stage_all[wave][0][j * kWave + lane] = sv[0][j];
         }
-        if (owns) *out_v = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+        u32x4 nv[R][L], ov[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ov[r] = u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
+            if (slot[r] >= 0) {
+                u32x4 *stage = stage_all[wave][r];
+                // coalesced chunk order -> per-lane channel order
+                wave_lds_sync();
+                uint32_t hist[4 * L];
+#pragma unroll
+                for (int k = 0; k < L; ++k) {
+                    const u32x4 t = stage[lane * L + k];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hist[4 * k + q] = t[q];
+                }
+                uint32_t xw[4] = {xv[r][0], xv[r][1], xv[r][2], xv[r][3]};
+                uint32_t outw[4], nhist[4 * L];
+                update8<L, ACT>(hist, xw, wf, bf, has_bias, outw, nhist);
+                ov[r] = u32x4{outw[0], outw[1], outw[2], outw[3]};
+                // per-lane channel order -> coalesced chunk order
+                wave_lds_sync();
+#pragma unroll
+                for (int k = 0; k < L; ++k)
+                    stage[lane * L + k] = u32x4{nhist[4 * k], nhist[4 * k + 1], nhist[4 * k + 2], nhist[4 * k + 3]};
+                wave_lds_sync();
+#pragma unroll
+                for (int j = 0; j < L; ++j) nv[r][j] = stage[j * kWave + lane];
+            }
+            if (r + 1 < R && slot[r + 1] >= 0) {
+#pragma unroll
+                for (int j = 0; j < L; ++j) stage_all[wave][r + 1][j * kWave + lane] = sv[r + 1][j];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all stores below, after all of the above
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (slot[r] == -2) break;  // no rows past this one either
+            if (slot[r] >= 0) {
+#pragma unroll
+                for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[r][j], sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+            }
+            const int row = group * R + r;
+            const Buffer obuf = make_buffer(p.out + (int64_t)row * p.d + c0, vec_bytes);
+            buffer_store<kStream>(ov[r], obuf, lane_bytes);
+        }
         wave_lds_sync();  // the stage is reused by the next unit
     }
 }
@@ -248,71 +346,64 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
         const int c0 = (int)(unit - (int64_t)row * tiles_per_row) * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const bool owns = lane < lanes_used;
-        uint4 *out_v = reinterpret_cast<uint4 *>(p.out + (int64_t)row * p.d + c0) + lane;
+        uint16_t *out_row = p.out + (int64_t)row * p.d + c0 + lane * kChPerLane;
 
         const int slot = route_row(p, row, lane);
         if (!owns) continue;
         if (slot < 0) {
-            *out_v = make_uint4(0u, 0u, 0u, 0u);
+            store_stream(out_row, u32x4{0u, 0u, 0u, 0u});
             continue;
         }
         const int c = c0 + lane * kChPerLane;
         const int L = p.l;
         uint16_t *base = p.state + (int64_t)slot * p.st_s + c;  // plane k at base + k * st_l
-        // The dot product needs planes L-3..L-1; the shift needs planes 1..L-1.
-        const uint4 xv = *reinterpret_cast<const uint4 *>(p.x + (int64_t)row * p.ld + c);
-        const uint4 *wp = reinterpret_cast<const uint4 *>(p.weight + (int64_t)c * 4);
-        uint4 wv[4];
+        // The taps read planes L-3..L-1 and x; the shift moves planes 1..L-1 down.
+        const u32x4 xv = load_stream(p.x + (int64_t)row * p.ld + c);
+        const u32x4 pa = load_stream(base + (int64_t)(L - 3) * p.st_l);
+        const u32x4 pb = load_stream(base + (int64_t)(L - 2) * p.st_l);
+        const u32x4 pc = load_stream(base + (int64_t)(L - 1) * p.st_l);
+        const uint16_t *wp = p.weight + (int64_t)c * 4;
+        u32x4 wv[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) wv[k] = wp[k];
+        for (int k = 0; k < 4; ++k) wv[k] = load_cached(wp + 8 * k);
         const bool has_bias = p.bias != nullptr;
-        const uint4 bv = has_bias ? *reinterpret_cast<const uint4 *>(p.bias + c) : make_uint4(0u, 0u, 0u, 0u);
-        uint4 p3 = *reinterpret_cast<const uint4 *>(base + (int64_t)(L - 3) * p.st_l);
-        uint4 p2 = *reinterpret_cast<const uint4 *>(base + (int64_t)(L - 2) * p.st_l);
-        uint4 p1 = *reinterpret_cast<const uint4 *>(base + (int64_t)(L - 1) * p.st_l);
+        const u32x4 bv = has_bias ? load_cached(p.bias + c) : u32x4{0u, 0u, 0u, 0u};
 
-        // Channel-major history of the 8 channels with L' = 3 (the three planes
-        // the taps read), so update8<3> does the arithmetic.
-        uint32_t hist[12], xw[4], ww[16], bw[4], outw[4], nhist[12];
-        uint32_t a[4], b[4], cc[4];
-        unpack4(p3, a); unpack4(p2, b); unpack4(p1, cc);
+        uint32_t outw[4];
+        float y[kChPerLane];
 #pragma unroll
         for (int ch = 0; ch < kChPerLane; ++ch) {
-            const uint32_t va = elem(a, ch), vb = elem(b, ch), vc = elem(cc, ch);
-            const int e = 3 * ch;
-            // place (va, vb, vc) at elements e, e+1, e+2
-            const uint32_t vals[3] = {va, vb, vc};
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int ei = e + k;
-                if (ei & 1) hist[ei >> 1] = (hist[ei >> 1] & 0xFFFFu) | (vals[k] << 16);
-                else hist[ei >> 1] = vals[k];
-            }
+            const int q = ch >> 1;
+            const bool h = ch & 1;
+            const u32x4 &w4 = wv[ch >> 1];
+            const int wq = (ch & 1) * 2;  // channel ch's taps: words 2*(ch&1), +1 of wv[ch>>1]
+            float acc = (h ? hi_f32(pa[q]) : lo_f32(pa[q])) * lo_f32(w4[wq]);
+            acc = __builtin_fmaf(h ? hi_f32(pb[q]) : lo_f32(pb[q]), hi_f32(w4[wq]), acc);
+            acc = __builtin_fmaf(h ? hi_f32(pc[q]) : lo_f32(pc[q]), lo_f32(w4[wq + 1]), acc);
+            acc = __builtin_fmaf(h ? hi_f32(xv[q]) : lo_f32(xv[q]), hi_f32(w4[wq + 1]), acc);
+            if (has_bias) acc += h ? hi_f32(bv[q]) : lo_f32(bv[q]);
+            y[ch] = activate<ACT>(acc);
         }
-        unpack4(xv, xw); unpack4(bv, bw);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) unpack4(wv[k], &ww[4 * k]);
-        update8<3, ACT>(hist, xw, ww, bw, has_bias, outw, nhist);
+        for (int i = 0; i < 4; ++i) outw[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
 
         // Shift: plane k <- plane k+1 for k < L-1, plane L-1 <- x.  Planes below
-        // L-3 are moved without being part of the arithmetic.
-        for (int k = 0; k < L - 3; ++k) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(base + (int64_t)(k + 1) * p.st_l);
-            *reinterpret_cast<uint4 *>(base + (int64_t)k * p.st_l) = v;
-        }
-        *reinterpret_cast<uint4 *>(base + (int64_t)(L - 3) * p.st_l) = p2;
-        *reinterpret_cast<uint4 *>(base + (int64_t)(L - 2) * p.st_l) = p1;
-        *reinterpret_cast<uint4 *>(base + (int64_t)(L - 1) * p.st_l) = xv;
-        *out_v = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+        // L-3 are moved without taking part in the arithmetic.
+        for (int k = 0; k < L - 3; ++k)
+            store_stream(base + (int64_t)k * p.st_l, load_stream(base + (int64_t)(k + 1) * p.st_l));
+        store_stream(base + (int64_t)(L - 3) * p.st_l, pb);
+        store_stream(base + (int64_t)(L - 2) * p.st_l, pc);
+        store_stream(base + (int64_t)(L - 1) * p.st_l, xv);
+        store_stream(out_row, u32x4{outw[0], outw[1], outw[2], outw[3]});
     }
 }
 
 template <int ACT>
-__global__ __launch_bounds__(kBlock) void update_scalar(UpdateParams p, int tiles_per_row, int64_t units) {
+__global__ __launch_bounds__(kScalarBlock) void update_scalar(UpdateParams p, int tiles_per_row, int64_t units) {
     const int lane = threadIdx.x & (kWave - 1);
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int row = (int)(unit / tiles_per_row);
-        const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarTile + (int)threadIdx.x;
+        const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
         const int slot = route_row(p, row, lane);
         if (c >= p.d) continue;
         uint16_t *o = p.out + (int64_t)row * p.d + c;
@@ -340,34 +431,55 @@ __global__ __launch_bounds__(kBlock) void update_scalar(UpdateParams p, int tile
 }
 
 template <typename Kernel>
-hipError_t launch(Kernel kernel, const UpdateParams &p, int tiles_per_row, int64_t units,
-                  int64_t units_per_block, hipStream_t stream) {
+hipError_t launch(Kernel kernel, const UpdateParams &p, int tiles_per_row, int64_t units, int units_per_block,
+                  int block, hipStream_t stream) {
     int64_t blocks = (units + units_per_block - 1) / units_per_block;
     if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     UpdateParams args_p = p;
     void *args[] = {&args_p, &tiles_per_row, &units};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(kBlock),
-                           args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(block), args, 0,
+                           stream);
+}
+
+template <int L, int ACT>
+hipError_t launch_compact_l(const UpdateParams &p, int tiles, hipStream_t stream, const char **name,
+                            const char *name_one_row, const char *name_two_rows) {
+    const int64_t waves_two_rows = (int64_t)((p.n + 1) / 2) * tiles;
+    if (p.n >= 2 && waves_two_rows >= kMinWavesForTwoRows) {
+        *name = name_two_rows;
+        return launch(update_compact_v8<L, ACT, 2>, p, tiles, waves_two_rows, kWavesPerBlock, kBlock, stream);
+    }
+    *name = name_one_row;
+    return launch(update_compact_v8<L, ACT, 1>, p, tiles, (int64_t)p.n * tiles, kWavesPerBlock, kBlock, stream);
 }
 
 template <int ACT>
-hipError_t launch_compact_v8(const UpdateParams &p, int tiles, int64_t units, hipStream_t stream,
-                             const char **name) {
-#define DCCONV_CASE(LL)                                                                  \
-    case LL:                                                                             \
-        *name = ACT ? "update_compact_v8<L=" #LL ",silu>" : "update_compact_v8<L=" #LL ",identity>"; \
-        return launch(update_compact_v8<LL, ACT>, p, tiles, units, kWavesPerBlock, stream);
-    switch (p.l) {
-        DCCONV_CASE(3)
-        DCCONV_CASE(4)
-        DCCONV_CASE(5)
-        DCCONV_CASE(6)
-        DCCONV_CASE(7)
-        DCCONV_CASE(8)
-        default:
-            return hipErrorInvalidValue;
+hipError_t launch_compact(const UpdateParams &p, int tiles, hipStream_t stream, const char **name) {
+#define DCCONV_COMPACT_CASE(LL, ACTNAME)                                                                   \
+    case LL:                                                                                               \
+        return launch_compact_l<LL, ACT>(p, tiles, stream, name, "update_compact_v8<L=" #LL "," ACTNAME ",R=1>", \
+                                         "update_compact_v8<L=" #LL "," ACTNAME ",R=2>");
+    if (ACT == DCCONV_ACT_SILU) {
+        switch (p.l) {
+            DCCONV_COMPACT_CASE(3, "silu")
+            DCCONV_COMPACT_CASE(4, "silu")
+            DCCONV_COMPACT_CASE(5, "silu")
+            DCCONV_COMPACT_CASE(6, "silu")
+            DCCONV_COMPACT_CASE(7, "silu")
+            DCCONV_COMPACT_CASE(8, "silu")
+            default: return hipErrorInvalidValue;
+        }
     }
-#undef DCCONV_CASE
+    switch (p.l) {
+        DCCONV_COMPACT_CASE(3, "identity")
+        DCCONV_COMPACT_CASE(4, "identity")
+        DCCONV_COMPACT_CASE(5, "identity")
+        DCCONV_COMPACT_CASE(6, "identity")
+        DCCONV_COMPACT_CASE(7, "identity")
+        DCCONV_COMPACT_CASE(8, "identity")
+        default: return hipErrorInvalidValue;
+    }
+#undef DCCONV_COMPACT_CASE
 }
 
 }  // namespace
@@ -376,24 +488,23 @@ hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activati
                          const char **kernel_name) {
     const bool rows_v8 = (p.d % kChPerLane == 0) && (p.ld % kChPerLane == 0);
     const bool silu = activation == DCCONV_ACT_SILU;
+    const int tiles_v8 = (p.d + kChPerWave - 1) / kChPerWave;
     if (layout == StateLayout::Compact && rows_v8 && p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8) {
-        const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
-        const int64_t units = (int64_t)p.n * tiles;
-        return silu ? launch_compact_v8<DCCONV_ACT_SILU>(p, tiles, units, stream, kernel_name)
-                    : launch_compact_v8<DCCONV_ACT_IDENTITY>(p, tiles, units, stream, kernel_name);
+        return silu ? launch_compact<DCCONV_ACT_SILU>(p, tiles_v8, stream, kernel_name)
+                    : launch_compact<DCCONV_ACT_IDENTITY>(p, tiles_v8, stream, kernel_name);
     }
     if (layout == StateLayout::ChannelLast && rows_v8 && p.st_s % kChPerLane == 0) {
-        const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
-        const int64_t units = (int64_t)p.n * tiles;
+        const int64_t units = (int64_t)p.n * tiles_v8;
         *kernel_name = silu ? "update_channel_last_v8<silu>" : "update_channel_last_v8<identity>";
-        return silu ? launch(update_channel_last_v8<DCCONV_ACT_SILU>, p, tiles, units, kWavesPerBlock, stream)
-                    : launch(update_channel_last_v8<DCCONV_ACT_IDENTITY>, p, tiles, units, kWavesPerBlock, stream);
+        return silu ? launch(update_channel_last_v8<DCCONV_ACT_SILU>, p, tiles_v8, units, kWavesPerBlock, kBlock, stream)
+                    : launch(update_channel_last_v8<DCCONV_ACT_IDENTITY>, p, tiles_v8, units, kWavesPerBlock, kBlock,
+                             stream);
     }
-    const int tiles = (p.d + kScalarTile - 1) / kScalarTile;
+    const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
     const int64_t units = (int64_t)p.n * tiles;
     *kernel_name = silu ? "update_scalar<silu>" : "update_scalar<identity>";
-    return silu ? launch(update_scalar<DCCONV_ACT_SILU>, p, tiles, units, 1, stream)
-                : launch(update_scalar<DCCONV_ACT_IDENTITY>, p, tiles, units, 1, stream);
+    return silu ? launch(update_scalar<DCCONV_ACT_SILU>, p, tiles, units, 1, kScalarBlock, stream)
+                : launch(update_scalar<DCCONV_ACT_IDENTITY>, p, tiles, units, 1, kScalarBlock, stream);
 }
 
 }  // namespace dcconv
