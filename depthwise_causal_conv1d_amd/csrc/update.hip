@@ -208,18 +208,22 @@ __device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uin
     }
 }
 
-template <int L, int ACT, int R>
+template <int L, int ACT, int R, bool HAS_BIAS>
 __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int tiles_per_row,
-                                                            int64_t units) {
+                                                            int64_t block_units) {
     __shared__ u32x4 stage_all[kWavesPerBlock][R][kWave * L];
+    __shared__ u32x4 weight_tile[4 * kWave];  // the tile's 4 KiB of weights, swizzled
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane_bytes = (uint32_t)lane * 16u;  // this lane's 16-byte vector in a 512-channel run
 
-    for (int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + wave; unit < units;
-         unit += (int64_t)gridDim.x * kWavesPerBlock) {
-        const int group = (int)(unit / tiles_per_row);
-        const int c0 = (int)(unit - (int64_t)group * tiles_per_row) * kChPerWave;
+    // A block owns one 512-channel tile and kWavesPerBlock groups of R rows, one
+    // group per wave, so the tile's weights are fetched once per block with
+    // coalesced loads and shared through LDS.
+    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+        const int tile = (int)(bu % tiles_per_row);
+        const int group = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;  // x / out / bias bytes of the tile
 
@@ -234,20 +238,22 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p, row, lane) : -2);
         }
 
-        // Issue every load up front: weights and bias once, then each row's x and
-        // state run.  Buffer descriptors bound each access: a row that must not
-        // touch memory gets an empty descriptor (its loads return zeros, its
-        // stores are dropped) and the lanes past a ragged tile's end fall outside
-        // the descriptor.  No load sits under a branch, so the compiler waits for
-        // each row's own data only.
-        const bool has_bias = p.bias != nullptr;
+        // Issue every load up front: this wave's share of the weight tile, the
+        // bias, then each row's x and state run.  Buffer descriptors bound each
+        // access: a row that must not touch memory gets empty descriptors (its
+        // loads return zeros, its stores are dropped) and the lanes past a ragged
+        // tile's end fall outside the descriptor.  Nothing below branches on the
+        // row, so the compiler can wait for each row's own loads only.
+        __builtin_amdgcn_s_setprio(3);  // get the loads of every wave queued early
         const Buffer wbuf = make_buffer(p.weight + (int64_t)c0 * 4, vec_bytes * 4u);
-        const Buffer bbuf = make_buffer(has_bias ? p.bias + c0 : p.weight, has_bias ? vec_bytes : 0u);
-        u32x4 wv[4];
+        constexpr int kWeightChunks = 4 / kWavesPerBlock;  // 1-KiB pieces of the tile per wave
+        u32x4 wraw[kWeightChunks];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) wv[k] = buffer_load<kCached>(wbuf, lane_bytes * 4u + 16u * k);
-        const u32x4 bv = buffer_load<kCached>(bbuf, lane_bytes);
-        Buffer sbuf[R];
+        for (int q = 0; q < kWeightChunks; ++q)
+            wraw[q] = buffer_load<kCached>(wbuf, (uint32_t)((wave * kWeightChunks + q) * 1024) + lane_bytes);
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        Buffer sbuf[R], obuf[R];
         u32x4 xv[R], sv[R][L];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -256,17 +262,32 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u);
             sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + (int64_t)c0 * L : p.x,
                                   live ? vec_bytes * L : 0u);
+            obuf[r] = make_buffer(p.out + (int64_t)row * p.d + c0, slot[r] != -2 ? vec_bytes : 0u);
             xv[r] = buffer_load<kStream>(xbuf, lane_bytes);
 #pragma unroll
             for (int j = 0; j < L; ++j) sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
         }
+        __builtin_amdgcn_s_setprio(0);
+
+        // Weight tile: 16-byte unit u holds lane u/4's taps for channels
+        // 2(u%4), 2(u%4)+1 of its 8.  It is stored at u ^ ((u >> 4) & 3), which keeps
+        // both the coalesced writes and the per-lane reads (stride 64 bytes) free of
+        // LDS bank conflicts.
+#pragma unroll
+        for (int q = 0; q < kWeightChunks; ++q) {
+            const int u = (wave * kWeightChunks + q) * kWave + lane;
+            weight_tile[u ^ ((u >> 4) & 3)] = wraw[q];
+        }
+        __syncthreads();
         float wf[32], bf[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+            const int u = 4 * lane + k;
+            const u32x4 wk = weight_tile[u ^ ((u >> 4) & 3)];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                wf[8 * k + 2 * q] = lo_f32(wv[k][q]);
-                wf[8 * k + 2 * q + 1] = hi_f32(wv[k][q]);
+                wf[8 * k + 2 * q] = lo_f32(wk[q]);
+                wf[8 * k + 2 * q + 1] = hi_f32(wk[q]);
             }
         }
 #pragma unroll
@@ -282,39 +303,35 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
         // (for the next row's loads, or for a register the store still holds)
         // would also wait for that store to be acknowledged by memory.  Keeping
         // all stores last means no wait ever follows one.
-        if (slot[0] >= 0) {
 #pragma unroll
-            for (int j = 0; j < L; ++j) stage_all[wave][0][j * kWave + lane] = sv[0][j];
-        }
+        for (int j = 0; j < L; ++j) stage_all[wave][0][j * kWave + lane] = sv[0][j];
         u32x4 nv[R][L], ov[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            ov[r] = u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
-            if (slot[r] >= 0) {
-                u32x4 *stage = stage_all[wave][r];
-                // coalesced chunk order -> per-lane channel order
-                wave_lds_sync();
-                uint32_t hist[4 * L];
+            u32x4 *stage = stage_all[wave][r];
+            // coalesced chunk order -> per-lane channel order
+            wave_lds_sync();
+            uint32_t hist[4 * L];
 #pragma unroll
-                for (int k = 0; k < L; ++k) {
-                    const u32x4 t = stage[lane * L + k];
+            for (int k = 0; k < L; ++k) {
+                const u32x4 t = stage[lane * L + k];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) hist[4 * k + q] = t[q];
-                }
-                uint32_t xw[4] = {xv[r][0], xv[r][1], xv[r][2], xv[r][3]};
-                uint32_t outw[4], nhist[4 * L];
-                update8<L, ACT>(hist, xw, wf, bf, has_bias, outw, nhist);
-                ov[r] = u32x4{outw[0], outw[1], outw[2], outw[3]};
-                // per-lane channel order -> coalesced chunk order
-                wave_lds_sync();
-#pragma unroll
-                for (int k = 0; k < L; ++k)
-                    stage[lane * L + k] = u32x4{nhist[4 * k], nhist[4 * k + 1], nhist[4 * k + 2], nhist[4 * k + 3]};
-                wave_lds_sync();
-#pragma unroll
-                for (int j = 0; j < L; ++j) nv[r][j] = stage[j * kWave + lane];
+                for (int q = 0; q < 4; ++q) hist[4 * k + q] = t[q];
             }
-            if (r + 1 < R && slot[r + 1] >= 0) {
+            uint32_t xw[4] = {xv[r][0], xv[r][1], xv[r][2], xv[r][3]};
+            uint32_t outw[4], nhist[4 * L];
+            update8<L, ACT>(hist, xw, wf, bf, HAS_BIAS, outw, nhist);
+            const bool live = slot[r] >= 0;  // a padding row writes zeros
+            ov[r] = u32x4{live ? outw[0] : 0u, live ? outw[1] : 0u, live ? outw[2] : 0u, live ? outw[3] : 0u};
+            // per-lane channel order -> coalesced chunk order
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+                stage[lane * L + k] = u32x4{nhist[4 * k], nhist[4 * k + 1], nhist[4 * k + 2], nhist[4 * k + 3]};
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < L; ++j) nv[r][j] = stage[j * kWave + lane];
+            if (r + 1 < R) {
 #pragma unroll
                 for (int j = 0; j < L; ++j) stage_all[wave][r + 1][j * kWave + lane] = sv[r + 1][j];
             }
@@ -322,16 +339,11 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
         __builtin_amdgcn_sched_barrier(0);  // all stores below, after all of the above
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (slot[r] == -2) break;  // no rows past this one either
-            if (slot[r] >= 0) {
 #pragma unroll
-                for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[r][j], sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
-            }
-            const int row = group * R + r;
-            const Buffer obuf = make_buffer(p.out + (int64_t)row * p.d + c0, vec_bytes);
-            buffer_store<kStream>(ov[r], obuf, lane_bytes);
+            for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[r][j], sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+            buffer_store<kStream>(ov[r], obuf[r], lane_bytes);
         }
-        wave_lds_sync();  // the stage is reused by the next unit
+        __syncthreads();  // the stages and the weight tile are reused by the next unit
     }
 }
 
@@ -444,13 +456,18 @@ hipError_t launch(Kernel kernel, const UpdateParams &p, int tiles_per_row, int64
 template <int L, int ACT>
 hipError_t launch_compact_l(const UpdateParams &p, int tiles, hipStream_t stream, const char **name,
                             const char *name_one_row, const char *name_two_rows) {
-    const int64_t waves_two_rows = (int64_t)((p.n + 1) / 2) * tiles;
-    if (p.n >= 2 && waves_two_rows >= kMinWavesForTwoRows) {
+    const bool bias = p.bias != nullptr;
+    const int64_t groups_two = (p.n + 1) / 2;
+    if (p.n >= 2 && groups_two * tiles >= kMinWavesForTwoRows) {
         *name = name_two_rows;
-        return launch(update_compact_v8<L, ACT, 2>, p, tiles, waves_two_rows, kWavesPerBlock, kBlock, stream);
+        const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
+        return bias ? launch(update_compact_v8<L, ACT, 2, true>, p, tiles, block_units, 1, kBlock, stream)
+                    : launch(update_compact_v8<L, ACT, 2, false>, p, tiles, block_units, 1, kBlock, stream);
     }
     *name = name_one_row;
-    return launch(update_compact_v8<L, ACT, 1>, p, tiles, (int64_t)p.n * tiles, kWavesPerBlock, kBlock, stream);
+    const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
+    return bias ? launch(update_compact_v8<L, ACT, 1, true>, p, tiles, block_units, 1, kBlock, stream)
+                : launch(update_compact_v8<L, ACT, 1, false>, p, tiles, block_units, 1, kBlock, stream);
 }
 
 template <int ACT>
