@@ -103,7 +103,8 @@ class Workload:
         self.set_bytes = set_bytes
         active = spec.N if data["indices"] is None else int((data["indices"] >= 0).sum())
         self.bytes_per_call = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active,
-                                                   data["bias"] is not None, data["indices"] is not None)
+                                                   data["bias"] is not None, data["indices"] is not None,
+                                                   spec.layout)
 
     def step(self, i: int):
         import depthwise_causal_conv1d_amd as dc
@@ -178,7 +179,7 @@ def cpu_baseline(spec, host, seconds: float):
         reps += 1
     active = spec.N if host["indices"] is None else int((host["indices"] >= 0).sum())
     b = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active, host["bias"] is not None,
-                             host["indices"] is not None)
+                             host["indices"] is not None, spec.layout)
     per_call = t_total / reps
     return {"value": b / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}) on host "
@@ -259,7 +260,7 @@ def main():
         f"{res['buffer_sets']} buffer sets, wall {res['wall_ms_per_step'] * 1e3:.3f} us/step")
     others = []
     if not args.no_other_workloads:
-        for other in wl.CONFIGS:
+        for other in wl.CONFIGS + wl.EXTRA:
             if other.name == spec.name:
                 continue
             r, _ = measure(other, max(200, args.steps // 5), 20, min(args.rotate_mb, 512.0), args.launch)

@@ -24,10 +24,12 @@
 //    The single-use streams (x, state, out) carry the non-temporal hint, which
 //    keeps them from displacing the reused weights and routing table in the
 //    caches.
-//  * update_channel_last_v8<ACT>: the [S, L, D] layout a prefill hands over.
-//    Every history position is a contiguous plane over channels, so the lane that
-//    owns 8 channels loads and stores each plane with one coalesced 16-byte
-//    access and the shift is a plane renaming; no LDS is needed.
+//  * update_channel_last_v8<L, ACT, R>: the [S, L, D] layout a prefill hands
+//    over.  Every history position is a contiguous plane over channels, so the
+//    lane that owns 8 channels loads and stores each plane with one coalesced
+//    16-byte access and the shift is a renaming of planes; no state goes through
+//    LDS, and position 0 is not read unless it is a tap (L = 3).  The same block
+//    structure, weight sharing and store ordering as the compact kernel.
 //  * update_scalar<ACT>: one thread per (row, channel), any stride, any L >= 3,
 //    any D.  Serves what the vector paths do not (D or row stride not a multiple
 //    of 8, L > 8).
@@ -347,66 +349,120 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
     }
 }
 
-template <int ACT>
+template <int L, int ACT, int R, bool HAS_BIAS>
 __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p, int tiles_per_row,
-                                                                 int64_t units) {
+                                                                 int64_t block_units) {
+    __shared__ u32x4 weight_tile[4 * kWave];
+    // Planes the update reads: the taps need positions L-3..L-1, the shift needs
+    // 1..L-1; position 0 is only read when it is also a tap (L = 3).
+    constexpr int kFirst = L == 3 ? 0 : 1;
+    constexpr int kRead = L - kFirst;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    for (int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + wave; unit < units;
-         unit += (int64_t)gridDim.x * kWavesPerBlock) {
-        const int row = (int)(unit / tiles_per_row);
-        const int c0 = (int)(unit - (int64_t)row * tiles_per_row) * kChPerWave;
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const uint32_t plane_bytes = (uint32_t)p.st_l * 2u;  // distance between history positions
+
+    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+        const int tile = (int)(bu % tiles_per_row);
+        const int group = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
-        const bool owns = lane < lanes_used;
-        uint16_t *out_row = p.out + (int64_t)row * p.d + c0 + lane * kChPerLane;
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+        // One descriptor spans a row's L planes of this tile; a lane past a ragged
+        // tile's end gets an offset beyond every descriptor (2^31 > its size), so
+        // it can neither read nor write a neighbouring plane.
+        const uint32_t plane_lane = lane < lanes_used ? lane_bytes : 0x80000000u;
 
-        const int slot = route_row(p, row, lane);
-        if (!owns) continue;
-        if (slot < 0) {
-            store_stream(out_row, u32x4{0u, 0u, 0u, 0u});
-            continue;
+        int slot[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = group * R + r;
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p, row, lane) : -2);
         }
-        const int c = c0 + lane * kChPerLane;
-        const int L = p.l;
-        uint16_t *base = p.state + (int64_t)slot * p.st_s + c;  // plane k at base + k * st_l
-        // The taps read planes L-3..L-1 and x; the shift moves planes 1..L-1 down.
-        const u32x4 xv = load_stream(p.x + (int64_t)row * p.ld + c);
-        const u32x4 pa = load_stream(base + (int64_t)(L - 3) * p.st_l);
-        const u32x4 pb = load_stream(base + (int64_t)(L - 2) * p.st_l);
-        const u32x4 pc = load_stream(base + (int64_t)(L - 1) * p.st_l);
-        const uint16_t *wp = p.weight + (int64_t)c * 4;
-        u32x4 wv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wv[k] = load_cached(wp + 8 * k);
-        const bool has_bias = p.bias != nullptr;
-        const u32x4 bv = has_bias ? load_cached(p.bias + c) : u32x4{0u, 0u, 0u, 0u};
 
-        uint32_t outw[4];
-        float y[kChPerLane];
+        __builtin_amdgcn_s_setprio(3);
+        const Buffer wbuf = make_buffer(p.weight + (int64_t)c0 * 4, vec_bytes * 4u);
+        constexpr int kWeightChunks = 4 / kWavesPerBlock;
+        u32x4 wraw[kWeightChunks];
 #pragma unroll
-        for (int ch = 0; ch < kChPerLane; ++ch) {
-            const int q = ch >> 1;
-            const bool h = ch & 1;
-            const u32x4 &w4 = wv[ch >> 1];
-            const int wq = (ch & 1) * 2;  // channel ch's taps: words 2*(ch&1), +1 of wv[ch>>1]
-            float acc = (h ? hi_f32(pa[q]) : lo_f32(pa[q])) * lo_f32(w4[wq]);
-            acc = __builtin_fmaf(h ? hi_f32(pb[q]) : lo_f32(pb[q]), hi_f32(w4[wq]), acc);
-            acc = __builtin_fmaf(h ? hi_f32(pc[q]) : lo_f32(pc[q]), lo_f32(w4[wq + 1]), acc);
-            acc = __builtin_fmaf(h ? hi_f32(xv[q]) : lo_f32(xv[q]), hi_f32(w4[wq + 1]), acc);
-            if (has_bias) acc += h ? hi_f32(bv[q]) : lo_f32(bv[q]);
-            y[ch] = activate<ACT>(acc);
+        for (int q = 0; q < kWeightChunks; ++q)
+            wraw[q] = buffer_load<kCached>(wbuf, (uint32_t)((wave * kWeightChunks + q) * 1024) + lane_bytes);
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        Buffer sbuf[R], obuf[R];
+        u32x4 xv[R], pv[R][kRead];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool live = slot[r] >= 0;
+            const int row = min(group * R + r, p.n - 1);
+            const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u);
+            sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + c0 : p.x,
+                                  live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+            obuf[r] = make_buffer(p.out + (int64_t)row * p.d + c0, slot[r] != -2 ? vec_bytes : 0u);
+            xv[r] = buffer_load<kStream>(xbuf, lane_bytes);
+#pragma unroll
+            for (int k = 0; k < kRead; ++k)
+                pv[r][k] = buffer_load<kStream>(sbuf[r], plane_bytes * (uint32_t)(kFirst + k) + plane_lane);
+        }
+        __builtin_amdgcn_s_setprio(0);
+
+#pragma unroll
+        for (int q = 0; q < kWeightChunks; ++q) {
+            const int u = (wave * kWeightChunks + q) * kWave + lane;
+            weight_tile[u ^ ((u >> 4) & 3)] = wraw[q];
+        }
+        __syncthreads();
+        float wf[32], bf[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = 4 * lane + k;
+            const u32x4 wk = weight_tile[u ^ ((u >> 4) & 3)];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wf[8 * k + 2 * q] = lo_f32(wk[q]);
+                wf[8 * k + 2 * q + 1] = hi_f32(wk[q]);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) outw[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+        for (int q = 0; q < 4; ++q) {
+            bf[2 * q] = lo_f32(bv[q]);
+            bf[2 * q + 1] = hi_f32(bv[q]);
+        }
 
-        // Shift: plane k <- plane k+1 for k < L-1, plane L-1 <- x.  Planes below
-        // L-3 are moved without taking part in the arithmetic.
-        for (int k = 0; k < L - 3; ++k)
-            store_stream(base + (int64_t)k * p.st_l, load_stream(base + (int64_t)(k + 1) * p.st_l));
-        store_stream(base + (int64_t)(L - 3) * p.st_l, pb);
-        store_stream(base + (int64_t)(L - 2) * p.st_l, pc);
-        store_stream(base + (int64_t)(L - 1) * p.st_l, xv);
-        store_stream(out_row, u32x4{outw[0], outw[1], outw[2], outw[3]});
+        // Each plane vector already holds this lane's 8 channels at one history
+        // position, so the taps read planes L-3..L-1 directly and the shift is a
+        // renaming of planes.  All stores come last (see the compact kernel).
+        u32x4 ov[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 &pa = pv[r][L - 3 - kFirst], &pb = pv[r][L - 2 - kFirst], &pc = pv[r][L - 1 - kFirst];
+            float y[kChPerLane];
+#pragma unroll
+            for (int ch = 0; ch < kChPerLane; ++ch) {
+                const int q = ch >> 1;
+                const bool h = ch & 1;
+                float acc = (h ? hi_f32(pa[q]) : lo_f32(pa[q])) * wf[4 * ch + 0];
+                acc = __builtin_fmaf(h ? hi_f32(pb[q]) : lo_f32(pb[q]), wf[4 * ch + 1], acc);
+                acc = __builtin_fmaf(h ? hi_f32(pc[q]) : lo_f32(pc[q]), wf[4 * ch + 2], acc);
+                acc = __builtin_fmaf(h ? hi_f32(xv[r][q]) : lo_f32(xv[r][q]), wf[4 * ch + 3], acc);
+                if (HAS_BIAS) acc += bf[ch];
+                y[ch] = activate<ACT>(acc);
+            }
+            const bool live = slot[r] >= 0;  // a padding row writes zeros
+            ov[r] = u32x4{live ? pack_bf16x2(y[0], y[1]) : 0u, live ? pack_bf16x2(y[2], y[3]) : 0u,
+                          live ? pack_bf16x2(y[4], y[5]) : 0u, live ? pack_bf16x2(y[6], y[7]) : 0u};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            // plane k <- old plane k+1 (k < L-1), plane L-1 <- x
+#pragma unroll
+            for (int k = 0; k < L - 1; ++k)
+                buffer_store<kStream>(pv[r][k + 1 - kFirst], sbuf[r], plane_bytes * (uint32_t)k + plane_lane);
+            buffer_store<kStream>(xv[r], sbuf[r], plane_bytes * (uint32_t)(L - 1) + plane_lane);
+            buffer_store<kStream>(ov[r], obuf[r], lane_bytes);
+        }
+        __syncthreads();  // the weight tile is reused by the next unit
     }
 }
 
@@ -499,6 +555,53 @@ hipError_t launch_compact(const UpdateParams &p, int tiles, hipStream_t stream, 
 #undef DCCONV_COMPACT_CASE
 }
 
+template <int L, int ACT>
+hipError_t launch_channel_last_l(const UpdateParams &p, int tiles, hipStream_t stream, const char **name,
+                                 const char *name_one_row, const char *name_two_rows) {
+    const bool bias = p.bias != nullptr;
+    const int64_t groups_two = (p.n + 1) / 2;
+    if (p.n >= 2 && groups_two * tiles >= kMinWavesForTwoRows) {
+        *name = name_two_rows;
+        const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
+        return bias ? launch(update_channel_last_v8<L, ACT, 2, true>, p, tiles, block_units, 1, kBlock, stream)
+                    : launch(update_channel_last_v8<L, ACT, 2, false>, p, tiles, block_units, 1, kBlock, stream);
+    }
+    *name = name_one_row;
+    const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
+    return bias ? launch(update_channel_last_v8<L, ACT, 1, true>, p, tiles, block_units, 1, kBlock, stream)
+                : launch(update_channel_last_v8<L, ACT, 1, false>, p, tiles, block_units, 1, kBlock, stream);
+}
+
+template <int ACT>
+hipError_t launch_channel_last(const UpdateParams &p, int tiles, hipStream_t stream, const char **name) {
+#define DCCONV_CL_CASE(LL, ACTNAME)                                                                          \
+    case LL:                                                                                                  \
+        return launch_channel_last_l<LL, ACT>(p, tiles, stream, name,                                         \
+                                              "update_channel_last_v8<L=" #LL "," ACTNAME ",R=1>",            \
+                                              "update_channel_last_v8<L=" #LL "," ACTNAME ",R=2>");
+    if (ACT == DCCONV_ACT_SILU) {
+        switch (p.l) {
+            DCCONV_CL_CASE(3, "silu")
+            DCCONV_CL_CASE(4, "silu")
+            DCCONV_CL_CASE(5, "silu")
+            DCCONV_CL_CASE(6, "silu")
+            DCCONV_CL_CASE(7, "silu")
+            DCCONV_CL_CASE(8, "silu")
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (p.l) {
+        DCCONV_CL_CASE(3, "identity")
+        DCCONV_CL_CASE(4, "identity")
+        DCCONV_CL_CASE(5, "identity")
+        DCCONV_CL_CASE(6, "identity")
+        DCCONV_CL_CASE(7, "identity")
+        DCCONV_CL_CASE(8, "identity")
+        default: return hipErrorInvalidValue;
+    }
+#undef DCCONV_CL_CASE
+}
+
 }  // namespace
 
 hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation, hipStream_t stream,
@@ -510,12 +613,10 @@ hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activati
         return silu ? launch_compact<DCCONV_ACT_SILU>(p, tiles_v8, stream, kernel_name)
                     : launch_compact<DCCONV_ACT_IDENTITY>(p, tiles_v8, stream, kernel_name);
     }
-    if (layout == StateLayout::ChannelLast && rows_v8 && p.st_s % kChPerLane == 0) {
-        const int64_t units = (int64_t)p.n * tiles_v8;
-        *kernel_name = silu ? "update_channel_last_v8<silu>" : "update_channel_last_v8<identity>";
-        return silu ? launch(update_channel_last_v8<DCCONV_ACT_SILU>, p, tiles_v8, units, kWavesPerBlock, kBlock, stream)
-                    : launch(update_channel_last_v8<DCCONV_ACT_IDENTITY>, p, tiles_v8, units, kWavesPerBlock, kBlock,
-                             stream);
+    if (layout == StateLayout::ChannelLast && rows_v8 && p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8 &&
+        (int64_t)p.l * p.st_l * 2 < (int64_t)1 << 30) {
+        return silu ? launch_channel_last<DCCONV_ACT_SILU>(p, tiles_v8, stream, kernel_name)
+                    : launch_channel_last<DCCONV_ACT_IDENTITY>(p, tiles_v8, stream, kernel_name);
     }
     const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
     const int64_t units = (int64_t)p.n * tiles;

@@ -60,7 +60,14 @@ CONFIGS = [
     Spec("long_history", N=128, D=4096, W=4, L=8, S=1024, ld=4096, bias=True, act=None,
          routing="unique", T=16, seed=5),
 ]
-BY_NAME = {c.name: c for c in CONFIGS}
+# Further workloads the benchmark reports beside the five (not parity configurations):
+# the large decode batch with its state handed over channel-last, as a prefill
+# leaves it.
+EXTRA = [
+    Spec("large_decode_channel_last", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
+         routing="none", weight_dist="uniform", seed=4, layout="channel_last"),
+]
+BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -124,10 +131,16 @@ def state_strides(spec: Spec):
 
 
 def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bool,
-                      indices: bool) -> int:
+                      indices: bool, layout: str = "compact") -> int:
     """Bytes one decode call must move at minimum: x and the selected state read,
     the state written back (the history shifts, so all L values are rewritten),
-    weight, bias, output, index table.  Padding rows read no x and no state."""
+    weight, bias, output, index table.  Padding rows read no x and no state.
+
+    State read: in the compact layout a channel's L values are adjacent, so all L
+    are read.  Channel-last keeps each history position in its own plane, and
+    position 0 is only needed when it is also a tap (L == W - 1 = 3), so
+    max(W - 1, L - 1) positions are read."""
     A = active_rows
-    return (2 * A * D + 2 * A * D * L + 2 * A * D * L + 2 * D * W
+    read_positions = L if layout == "compact" else max(W - 1, L - 1)
+    return (2 * A * D + 2 * A * D * read_positions + 2 * A * D * L + 2 * D * W
             + (2 * D if bias else 0) + 2 * N * D + (4 * N if indices else 0))

@@ -124,6 +124,35 @@ def test_channel_last_layout(L, act):
     assert "channel_last_v8" in case.kernel
 
 
+@pytest.mark.parametrize("L", [5, 7, 8])
+def test_channel_last_more_l(L):
+    case = make_case(320 + L, N=5, D=1544, L=L, S=9, layout="channel_last", routing="unique", bias=False, act="silu")
+    case.check()
+    assert "channel_last_v8" in case.kernel
+
+
+@pytest.mark.parametrize("layout", ["compact", "channel_last"])
+@pytest.mark.parametrize("act", [None, "silu"])
+def test_two_rows_per_wave_odd_n_padding_bias(layout, act):
+    """N odd (the last wave has one row and one row past the end), padding rows
+    inside row pairs, a bias, an index table, a ragged tile: the two-row kernels."""
+    case = make_case(330, N=131, D=8200, L=3, S=300, layout=layout, routing="padded", n_pad=17, bias=True, act=act,
+                     status=True)
+    assert case.check() == 0
+    assert "R=2" in case.kernel, case.kernel
+
+
+def test_channel_last_full_size_large_decode():
+    """The large decode shape (N=256, D=8192, L=3, ld=8200, SiLU) with the state
+    handed over channel-last, checked element by element."""
+    spec = wl.Spec("large_decode_cl", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
+                   routing="none", weight_dist="uniform", seed=4, layout="channel_last")
+    data = wl.make(spec)
+    case = Case(data["x"][0], spec.D, data["weight"], data["state"], layout="channel_last", act="silu")
+    case.check()
+    assert case.kernel == "update_channel_last_v8<L=3,silu,R=2>"
+
+
 def test_channel_last_scalar_path():
     case = make_case(310, N=4, D=21, L=3, S=4, layout="channel_last", act="silu")
     case.check()
