@@ -59,6 +59,11 @@ def lib() -> ctypes.CDLL:
             L.oracle_update.restype = i32
             L.oracle_update.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64,
                                         vp, i64, vp, vp, i32, vp, vp]
+            L.oracle_update_tokens.restype = i32
+            L.oracle_update_tokens.argtypes = [vp, i64, i64, i64, i64, i64, i64,   # x, n, d, t, xs_n, xs_d, xs_t
+                                               vp, i64, i64, i64, i64, i64,        # state, s, l, st_s, st_d, st_l
+                                               vp, i64, vp, vp, i32,               # weight, w, bias, indices, act
+                                               vp, vp, i64, i64, i64]              # out, out_f32, os_n, os_d, os_t
             L.oracle_bf16_to_f32.restype = ctypes.c_float
             L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
             L.oracle_f32_to_bf16.restype = ctypes.c_uint16
@@ -141,6 +146,27 @@ def update_strided(x, n, d, ld, state_buf, S, L, strides, weight, bias, indices,
     rc = lib().oracle_update(_ptr(x), n, d, ld, _ptr(state_buf), S, L, strides[0], strides[1],
                              strides[2], _ptr(weight), W, _ptr(bias), _ptr(indices),
                              ACT[activation], _ptr(out), _ptr(out_f32))
+    if rc != OK:
+        raise OracleError(rc)
+    return (out, out_f32) if want_f32 else out
+
+
+def update_tokens(x_buf, n, d, t, x_strides, state_buf, S, L, state_strides, weight, bias, indices,
+                  activation, want_f32=False):
+    """T successive decode steps (the multi-token form x[N, D, T]).
+
+    x_buf: flat/any-shape contiguous uint16 buffer holding x at element strides
+    ``x_strides`` = (n, channel, token); state_buf likewise at ``state_strides``.
+    Returns out as uint16 [N, T, D] (token-major), or (out, out_f32).
+    """
+    _need(x_buf, np.uint16, "x_buf"); _need(state_buf, np.uint16, "state_buf")
+    W = weight.shape[1]
+    out = np.zeros((n, t, d), dtype=np.uint16)
+    out_f32 = np.zeros((n, t, d), dtype=np.float32) if want_f32 else None
+    rc = lib().oracle_update_tokens(_ptr(x_buf), n, d, t, x_strides[0], x_strides[1], x_strides[2],
+                                    _ptr(state_buf), S, L, state_strides[0], state_strides[1], state_strides[2],
+                                    _ptr(weight), W, _ptr(bias), _ptr(indices), ACT[activation],
+                                    _ptr(out), _ptr(out_f32), t * d, 1, d)
     if rc != OK:
         raise OracleError(rc)
     return (out, out_f32) if want_f32 else out

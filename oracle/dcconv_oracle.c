@@ -58,6 +58,14 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+int oracle_update_tokens(const uint16_t *x, int64_t n_rows, int64_t d, int64_t t_steps,
+                         int64_t xs_n, int64_t xs_d, int64_t xs_t,
+                         uint16_t *state, int64_t s_slots, int64_t l,
+                         int64_t st_s, int64_t st_d, int64_t st_l,
+                         const uint16_t *weight, int64_t w, const uint16_t *bias,
+                         const int32_t *indices, int activation,
+                         uint16_t *out, float *out_f32, int64_t os_n, int64_t os_d, int64_t os_t);
+
 /* ---- helpers of the oracle itself ---- */
 
 static float act_apply(float acc, int activation)
@@ -99,6 +107,53 @@ static int resolve_slots(const int32_t *indices, int64_t n_rows, int64_t s_slots
 }
 
 /*
+ * The update of every row for one token (the body of the decode step below).
+ * x element (n, c) at x[n*xs_n + c*xs_d]; out element (n, c) at out[n*os_n + c*os_d];
+ * slot_of_row[n] already resolved (-1 = padding row).
+ */
+static void update_rows(const uint16_t *x, int64_t xs_n, int64_t xs_d, int64_t n_rows, int64_t d,
+                        uint16_t *state, int64_t l, int64_t st_s, int64_t st_d, int64_t st_l,
+                        const uint16_t *weight, int64_t w, const uint16_t *bias,
+                        const int64_t *slot_of_row, int activation,
+                        uint16_t *out, float *out_f32, int64_t os_n, int64_t os_d,
+                        float *hist, uint16_t *hist_bits)
+{
+    for (int64_t n = 0; n < n_rows; ++n) {
+        int64_t s = slot_of_row[n];
+        if (s == -1) {                       /* padding row: zero output, no mutation */
+            for (int64_t c = 0; c < d; ++c) {
+                out[n * os_n + c * os_d] = 0;
+                if (out_f32)
+                    out_f32[n * os_n + c * os_d] = 0.0f;
+            }
+            continue;
+        }
+        for (int64_t c = 0; c < d; ++c) {
+            uint16_t *slot = state + s * st_s + c * st_d;
+            /* history = concat(conv_state[s, c, :], x[n, c]) */
+            for (int64_t k = 0; k < l; ++k)
+                hist_bits[k] = slot[k * st_l];
+            hist_bits[l] = x[n * xs_n + c * xs_d];
+            /* conv_state[s, c, :] = history[-l:]  (a copy of bit patterns) */
+            for (int64_t k = 0; k < l; ++k)
+                slot[k * st_l] = hist_bits[k + 1];
+            for (int64_t k = 0; k <= l; ++k)
+                hist[k] = oracle_bf16_to_f32(hist_bits[k]);
+            /* acc = sum_j history[-w + j] * weight[c, j] + bias[c] */
+            float acc = 0.0f;
+            for (int64_t j = 0; j < w; ++j)
+                acc = acc + hist[l + 1 - w + j] * oracle_bf16_to_f32(weight[c * w + j]);
+            if (bias)
+                acc = acc + oracle_bf16_to_f32(bias[c]);
+            float y = act_apply(acc, activation);
+            if (out_f32)
+                out_f32[n * os_n + c * os_d] = y;
+            out[n * os_n + c * os_d] = oracle_f32_to_bf16(y);
+        }
+    }
+}
+
+/*
  * One decode step ("Causal Conv1d Decode Update" page, section of the same name).
  *
  *   x        BF16 bits [n_rows, d], element (n, c) at x[n*ld + c]
@@ -125,11 +180,34 @@ int oracle_update(const uint16_t *x, int64_t n_rows, int64_t d, int64_t ld,
                   const int32_t *indices, int activation,
                   uint16_t *out, float *out_f32)
 {
-    if (n_rows < 0 || d < 1 || s_slots < 0 || w < 1 || l < w - 1 || l < 1 || ld < d)
+    if (ld < d)
+        return ORACLE_EARGS;
+    return oracle_update_tokens(x, n_rows, d, 1, ld, 1, 0, state, s_slots, l, st_s, st_d, st_l,
+                                weight, w, bias, indices, activation, out, out_f32, d, 1, 0);
+}
+
+/*
+ * T successive decode steps on the same slots: the reading of the page's future
+ * multi-token form x[N, D, Tstep] ("Semantic tensor contract": the state and
+ * weight keep their meaning).  Token t of every row is applied, in order, by
+ * exactly the single-step rule above, and out[:, :, t] is that step's output.
+ *
+ *   x    element (n, c, t) at x[n*xs_n + c*xs_d + t*xs_t]
+ *   out  element (n, c, t) at out[n*os_n + c*os_d + t*os_t] (out_f32 the same)
+ */
+int oracle_update_tokens(const uint16_t *x, int64_t n_rows, int64_t d, int64_t t_steps,
+                         int64_t xs_n, int64_t xs_d, int64_t xs_t,
+                         uint16_t *state, int64_t s_slots, int64_t l,
+                         int64_t st_s, int64_t st_d, int64_t st_l,
+                         const uint16_t *weight, int64_t w, const uint16_t *bias,
+                         const int32_t *indices, int activation,
+                         uint16_t *out, float *out_f32, int64_t os_n, int64_t os_d, int64_t os_t)
+{
+    if (n_rows < 0 || d < 1 || t_steps < 0 || s_slots < 0 || w < 1 || l < w - 1 || l < 1)
         return ORACLE_EARGS;
     if (activation != ORACLE_ACT_IDENTITY && activation != ORACLE_ACT_SILU)
         return ORACLE_EARGS;
-    if (n_rows == 0)
+    if (n_rows == 0 || t_steps == 0)
         return ORACLE_OK;
     if (!x || !state || !weight || !out)
         return ORACLE_EARGS;
@@ -144,46 +222,14 @@ int oracle_update(const uint16_t *x, int64_t n_rows, int64_t d, int64_t ld,
         return ORACLE_EARGS;
     }
     int rc = resolve_slots(indices, n_rows, s_slots, slot_of_row);
-    if (rc != ORACLE_OK) {
-        free(slot_of_row); free(hist); free(hist_bits);
-        return rc;
-    }
-
-    for (int64_t n = 0; n < n_rows; ++n) {
-        int64_t s = slot_of_row[n];
-        if (s == -1) {                       /* padding row: zero output, no mutation */
-            for (int64_t c = 0; c < d; ++c) {
-                out[n * d + c] = 0;
-                if (out_f32)
-                    out_f32[n * d + c] = 0.0f;
-            }
-            continue;
-        }
-        for (int64_t c = 0; c < d; ++c) {
-            uint16_t *slot = state + s * st_s + c * st_d;
-            /* history = concat(conv_state[s, c, :], x[n, c]) */
-            for (int64_t k = 0; k < l; ++k)
-                hist_bits[k] = slot[k * st_l];
-            hist_bits[l] = x[n * ld + c];
-            /* conv_state[s, c, :] = history[-l:]  (a copy of bit patterns) */
-            for (int64_t k = 0; k < l; ++k)
-                slot[k * st_l] = hist_bits[k + 1];
-            for (int64_t k = 0; k <= l; ++k)
-                hist[k] = oracle_bf16_to_f32(hist_bits[k]);
-            /* acc = sum_j history[-w + j] * weight[c, j] + bias[c] */
-            float acc = 0.0f;
-            for (int64_t j = 0; j < w; ++j)
-                acc = acc + hist[l + 1 - w + j] * oracle_bf16_to_f32(weight[c * w + j]);
-            if (bias)
-                acc = acc + oracle_bf16_to_f32(bias[c]);
-            float y = act_apply(acc, activation);
-            if (out_f32)
-                out_f32[n * d + c] = y;
-            out[n * d + c] = oracle_f32_to_bf16(y);
-        }
+    if (rc == ORACLE_OK) {
+        for (int64_t t = 0; t < t_steps; ++t)
+            update_rows(x + t * xs_t, xs_n, xs_d, n_rows, d, state, l, st_s, st_d, st_l, weight, w, bias,
+                        slot_of_row, activation, out + t * os_t, out_f32 ? out_f32 + t * os_t : NULL,
+                        os_n, os_d, hist, hist_bits);
     }
     free(slot_of_row); free(hist); free(hist_bits);
-    return ORACLE_OK;
+    return rc;
 }
 
 /* Library self-description, so a loader can check it has the file it expects. */

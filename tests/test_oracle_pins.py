@@ -317,3 +317,60 @@ def test_row_stride_padding_is_never_read():
     out_c = oracle.update(np.ascontiguousarray(xp[:, :D]), st2, w, None, "silu")
     np.testing.assert_array_equal(out, out_c)
     np.testing.assert_array_equal(st, st2)
+
+
+# ------------------------------------------------------------- multi-token form
+
+
+@pytest.mark.parametrize("L", [3, 4, 8])
+@pytest.mark.parametrize("act", [None, "silu"])
+@pytest.mark.parametrize("x_layout", ["token_major", "channel_major"])
+def test_multi_token_equals_full_sequence_convolution(L, act, x_layout):
+    """x[N, D, T] applied as T successive steps == one float64 library causal
+    convolution over concat(state0, x_0..x_{T-1}); final state bit-exact."""
+    rng = np.random.default_rng(60 + L)
+    W, N, D, S, T = 4, 5, 11, 9, 6
+    idx = np.array([7, -1, 2, 0, -1], dtype=np.int32)
+    xt = rand_bf(rng, (N, T, D))                      # token-major values
+    if x_layout == "token_major":
+        xbuf, xs = np.ascontiguousarray(xt), (T * D, 1, D)
+    else:
+        xbuf, xs = np.ascontiguousarray(xt.transpose(0, 2, 1)), (D * T, T, 1)
+    w = rand_bf(rng, (D, W)); b = rand_bf(rng, (D,), 0.1)
+    state = rand_bf(rng, (S, D, L)); state0 = state.copy()
+    out, o32 = oracle.update_tokens(xbuf, N, D, T, xs, state, S, L, (D * L, L, 1), w, b, idx, act, want_f32=True)
+    for n, s in enumerate(idx):
+        if s < 0:
+            assert np.all(out[n] == 0)
+            continue
+        for c in range(D):
+            ext = np.concatenate([f64(state0[s, c]), f64(xt[n, :, c])])
+            full = conv_f64(ext, f64(w[c]))
+            bb = f64(b[c:c + 1])[0]
+            for t in range(T):
+                terms = np.abs(ext[L + t + 1 - W:L + t + 1]) @ np.abs(f64(w[c])) + abs(bb)
+                check_out(out[n, t, c:c + 1], o32[n, t, c:c + 1], np.array([full[L + t] + bb]), terms, act)
+            np.testing.assert_array_equal(state[s, c], np.concatenate([state0[s, c], xt[n, :, c]])[-L:])
+    untouched = [s for s in range(S) if s not in set(idx.tolist())]
+    np.testing.assert_array_equal(state[untouched], state0[untouched])
+
+
+def test_multi_token_with_one_token_is_the_single_step():
+    rng = np.random.default_rng(70)
+    N, D, L, S = 4, 24, 4, 6
+    x = rand_bf(rng, (N, D)); w = rand_bf(rng, (D, 4)); st = rand_bf(rng, (S, D, L))
+    idx = np.array([3, 0, -1, 5], dtype=np.int32)
+    s1, s2 = st.copy(), st.copy()
+    o1 = oracle.update(x, s1, w, None, "silu", conv_state_indices=idx)
+    o2 = oracle.update_tokens(x, N, D, 1, (D, 1, 0), s2, S, L, (D * L, L, 1), w, None, idx, "silu")
+    np.testing.assert_array_equal(o2[:, 0, :], o1)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_multi_token_longer_than_history_keeps_last_tokens():
+    """T > L: the state ends as the last L tokens, bit for bit."""
+    rng = np.random.default_rng(71)
+    N, D, L, T = 2, 8, 3, 9
+    xt = rand_bf(rng, (N, T, D)); w = rand_bf(rng, (D, 4)); st = rand_bf(rng, (N, D, L))
+    oracle.update_tokens(np.ascontiguousarray(xt), N, D, T, (T * D, 1, D), st, N, L, (D * L, L, 1), w, None, None, None)
+    np.testing.assert_array_equal(st, xt[:, T - L:, :].transpose(0, 2, 1))
