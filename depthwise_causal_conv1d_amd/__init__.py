@@ -10,7 +10,8 @@ HIP kernels.  PyTorch supplies device memory and the current stream.
 weight, bias, activation``, keyword-only ``cache_seqlens`` and
 ``conv_state_indices``; ``conv_state`` is updated in place and a newly allocated
 output is returned.  ``causal_conv1d_update_out`` writes into a caller buffer and
-allocates nothing.
+allocates nothing.  ``causal_conv1d_update_tokens`` applies T tokens per row in one
+call (the multi-token form x[N, D, T] the page reserves).
 
 There is no fallback: if the HIP library is missing, every call raises.
 """
@@ -24,7 +25,8 @@ __all__ = [
     "DCCONV_OK", "DCCONV_EINVAL", "DCCONV_EUNSUPPORTED", "DCCONV_EHIP",
     "DCCONV_ACT_IDENTITY", "DCCONV_ACT_SILU", "DCCONV_DEV_BAD_INDEX", "DCCONV_DEV_DUP_INDEX",
     "dcconv_abi_version", "dcconv_last_error", "dcconv_last_kernel", "dcconv_update",
-    "causal_conv1d_update", "causal_conv1d_update_out", "library_path", "DcconvError",
+    "dcconv_update_tokens", "causal_conv1d_update", "causal_conv1d_update_out",
+    "causal_conv1d_update_tokens", "library_path", "DcconvError",
 ]
 
 DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED, DCCONV_EHIP = 0, 1, 2, 3
@@ -71,6 +73,15 @@ def _load() -> ctypes.CDLL:
                                           vp, i64, vp,              # weight, w, bias
                                           vp, vp, i32,              # indices, cache_seqlens, activation
                                           vp, vp, vp]               # out, dev_status, stream
+            lib.dcconv_update_tokens.restype = i32
+            lib.dcconv_update_tokens.argtypes = [vp, i64, i64, i64,          # x, n, d, t
+                                                 i64, i64, i64,              # xs_n, xs_d, xs_t
+                                                 vp, i64, i64,               # conv_state, s, l
+                                                 i64, i64, i64,              # st_s, st_d, st_l
+                                                 vp, i64, vp,                # weight, w, bias
+                                                 vp, vp, i32,                # indices, cache_seqlens, activation
+                                                 vp, i64, i64, i64,          # out, os_n, os_d, os_t
+                                                 vp, vp]                     # dev_status, stream
             _lib = lib
     return _lib
 
@@ -110,6 +121,15 @@ def dcconv_update(x, n, d, ld_x, conv_state, s, l, st_s, st_d, st_l, weight, w, 
                                  dev_status, stream)
 
 
+def dcconv_update_tokens(x, n, d, t, xs_n, xs_d, xs_t, conv_state, s, l, st_s, st_d, st_l, weight, w, bias,
+                         conv_state_indices, cache_seqlens, activation, out, os_n, os_d, os_t, dev_status,
+                         stream) -> int:
+    """The multi-token C entry point, one to one (pointers as ints)."""
+    return _load().dcconv_update_tokens(x, n, d, t, xs_n, xs_d, xs_t, conv_state, s, l, st_s, st_d, st_l, weight,
+                                        w, bias, conv_state_indices, cache_seqlens, activation, out, os_n, os_d,
+                                        os_t, dev_status, stream)
+
+
 # ------------------------------------------------------------ tensor front end
 
 
@@ -117,7 +137,8 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation):
+def _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation,
+                   x_unit_channel_stride=True):
     import torch
 
     if cache_seqlens is not None:
@@ -145,7 +166,7 @@ def _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlen
     N, D = x.shape
     if conv_state.shape[1] != D or weight.shape[0] != D:
         raise ValueError(f"channel counts differ: x {D}, conv_state {conv_state.shape[1]}, weight {weight.shape[0]}")
-    if x.stride(1) != 1 and D > 1:
+    if x_unit_channel_stride and x.stride(1) != 1 and D > 1:
         raise ValueError("x must have unit stride along channels (strides (ld, 1))")
     if not weight.is_contiguous():
         raise ValueError("weight must be contiguous [D, W]")
@@ -198,3 +219,37 @@ def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None, *,
     out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     return causal_conv1d_update_out(x, conv_state, weight, bias, activation, out=out,
                                     conv_state_indices=conv_state_indices)
+
+
+def causal_conv1d_update_tokens(x, conv_state, weight, bias=None, activation=None, *, conv_state_indices=None,
+                                out=None, dev_status=None):
+    """T successive decode steps in one call: x is [N, D, T] (any strides), the
+    multi-token form the page reserves.  ``conv_state`` is updated in place (each
+    selected slot read and written once); returns out [N, D, T], by default
+    stored token-major (a view of a contiguous [N, T, D] buffer)."""
+    import torch
+
+    if x.dim() != 3:
+        raise ValueError(f"x must be [N, D, T], got shape {tuple(x.shape)}")
+    N, D, T = x.shape
+    x2 = x[:, :, 0] if T > 0 else x.new_empty(N, D)
+    _check_tensors(x2, conv_state, weight, bias, conv_state_indices, None, activation, x_unit_channel_stride=False)
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"x must be bfloat16, got {x.dtype}")
+    if out is None:
+        out = torch.empty(N, T, D, dtype=torch.bfloat16, device=x.device).permute(0, 2, 1)
+    elif out.shape != (N, D, T) or out.dtype != torch.bfloat16 or out.device != x.device:
+        raise ValueError("out must be a bfloat16 [N, D, T] tensor on x's device")
+    if dev_status is not None and (dev_status.dtype != torch.int32 or dev_status.device != x.device):
+        raise ValueError("dev_status must be an int32 tensor on x's device")
+    S, _, L = conv_state.shape
+    st = conv_state.stride()
+    xs, os_ = x.stride(), out.stride()
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = dcconv_update_tokens(_ptr(x), N, D, T, xs[0], xs[1], xs[2], _ptr(conv_state), S, L, st[0], st[1], st[2],
+                                  _ptr(weight), weight.shape[1], _ptr(bias), _ptr(conv_state_indices), None,
+                                  _ACTIVATIONS[activation], _ptr(out), os_[0], os_[1], os_[2], _ptr(dev_status),
+                                  stream)
+    _raise_for(rc)
+    return out

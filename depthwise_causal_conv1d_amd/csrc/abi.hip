@@ -53,6 +53,100 @@ bool overlaps(const Span &a, const Span &b) {
 
 constexpr int64_t kI32Max = 2147483647;
 
+
+// Metadata shared by both entry points: shapes, state strides, the served subset.
+int check_state_and_shapes(int64_t n, int64_t d, int64_t s, int64_t l, int64_t st_s, int64_t st_d, int64_t st_l,
+                           int64_t w, int activation, const int32_t *cache_seqlens, dcconv::StateLayout *layout) {
+    if (n < 0) return fail(DCCONV_EINVAL, "n (decode rows) must be >= 0, got %lld", (long long)n);
+    if (d < 1) return fail(DCCONV_EINVAL, "d (channels) must be >= 1, got %lld", (long long)d);
+    if (s < 0) return fail(DCCONV_EINVAL, "s (state slots) must be >= 0, got %lld", (long long)s);
+    if (w < 1) return fail(DCCONV_EINVAL, "w (filter width) must be >= 1, got %lld", (long long)w);
+    if (l < w - 1)
+        return fail(DCCONV_EINVAL, "conv_state length l=%lld must be >= w-1=%lld", (long long)l,
+                    (long long)(w - 1));
+    if (activation != DCCONV_ACT_IDENTITY && activation != DCCONV_ACT_SILU)
+        return fail(DCCONV_EINVAL, "activation must be DCCONV_ACT_IDENTITY (0) or DCCONV_ACT_SILU (1), got %d",
+                    activation);
+    if (st_s < 0 || st_d < 0 || st_l < 0) return fail(DCCONV_EINVAL, "conv_state strides must be non-negative");
+    if (cache_seqlens != nullptr)
+        return fail(DCCONV_EUNSUPPORTED,
+                    "cache_seqlens is reserved and must be NULL (circular-buffer state is not served)");
+    if (w != 4) return fail(DCCONV_EUNSUPPORTED, "only filter width w=4 is served, got w=%lld", (long long)w);
+    if (n > kI32Max || d > kI32Max || s > kI32Max || l > 65536)
+        return fail(DCCONV_EUNSUPPORTED, "sizes beyond n, d, s < 2^31 and l <= 65536 are not served");
+    if (st_l == 1 && st_d == l && (st_s >= d * l || s <= 1)) {
+        *layout = dcconv::StateLayout::Compact;
+    } else if (st_d == 1 && st_l == d && (st_s >= l * d || s <= 1)) {
+        *layout = dcconv::StateLayout::ChannelLast;
+    } else {
+        return fail(DCCONV_EUNSUPPORTED,
+                    "conv_state strides (%lld, %lld, %lld) are neither compact (>=d*l, l, 1) nor "
+                    "channel-last (>=l*d, 1, d)",
+                    (long long)st_s, (long long)st_d, (long long)st_l);
+    }
+    return DCCONV_OK;
+}
+
+// Pointers, alignment and overlap, once the byte extent of x and out is known.
+int check_pointers(const void *x, int64_t x_bytes, void *conv_state, int64_t s, int64_t d, int64_t l, int64_t st_s,
+                   int64_t st_d, int64_t st_l, const void *weight, int64_t w, const void *bias,
+                   const int32_t *conv_state_indices, int64_t n, void *out, int64_t out_bytes, int32_t *dev_status) {
+    if (!x || !weight || !out || (!conv_state && s > 0))
+        return fail(DCCONV_EINVAL, "x, weight, out (and conv_state when s > 0) must be non-NULL when n > 0");
+    if (conv_state_indices == nullptr && s < n)
+        return fail(DCCONV_EINVAL, "without conv_state_indices row r uses slot r, so s=%lld must be >= n=%lld",
+                    (long long)s, (long long)n);
+    if (!aligned(x, 16) || !aligned(conv_state, 16) || !aligned(weight, 16) || !aligned(out, 16) ||
+        (bias && !aligned(bias, 16)))
+        return fail(DCCONV_EINVAL, "BF16 tensors must be 16-byte aligned");
+    if ((conv_state_indices && !aligned(conv_state_indices, 4)) || (dev_status && !aligned(dev_status, 4)))
+        return fail(DCCONV_EINVAL, "conv_state_indices and dev_status must be 4-byte aligned");
+    // nothing the call writes may alias anything else it touches
+    const int64_t state_elems = s > 0 ? (s - 1) * st_s + (d - 1) * st_d + (l - 1) * st_l + 1 : 0;
+    const Span sx = span("x", x, x_bytes);
+    const Span sst = span("conv_state", conv_state, 2 * state_elems);
+    const Span sw = span("weight", weight, 2 * d * w);
+    const Span sb = span("bias", bias, 2 * d);
+    const Span si = span("conv_state_indices", conv_state_indices, 4 * n);
+    const Span so = span("out", out, out_bytes);
+    const Span ss = span("dev_status", dev_status, 4);
+    const Span written[] = {sst, so, ss};
+    const Span all[] = {sx, sst, sw, sb, si, so, ss};
+    for (const Span &a : written)
+        for (const Span &b : all)
+            if (a.name != b.name && overlaps(a, b))
+                return fail(DCCONV_EINVAL, "%s overlaps %s", a.name, b.name);
+    return DCCONV_OK;
+}
+
+// True when no two elements of an [e0, e1, e2] array at strides s0, s1, s2 share
+// an address: sorted by stride, each dimension must step over the whole extent of
+// the ones below it.
+bool strides_distinct(const int64_t e[3], const int64_t st[3]) {
+    int64_t ext[3], str[3];
+    int k = 0;
+    for (int i = 0; i < 3; ++i)
+        if (e[i] > 1) {
+            ext[k] = e[i];
+            str[k] = st[i];
+            ++k;
+        }
+    for (int i = 1; i < k; ++i)
+        for (int j = i; j > 0 && str[j] < str[j - 1]; --j) {
+            const int64_t te = ext[j], ts = str[j];
+            ext[j] = ext[j - 1];
+            str[j] = str[j - 1];
+            ext[j - 1] = te;
+            str[j - 1] = ts;
+        }
+    int64_t span_below = 1;
+    for (int i = 0; i < k; ++i) {
+        if (str[i] < span_below) return false;
+        span_below = str[i] * (ext[i] - 1) + span_below;
+    }
+    return true;
+}
+
 }  // namespace
 
 extern "C" int dcconv_abi_version(void) { return DCCONV_ABI_VERSION; }
@@ -72,75 +166,21 @@ extern "C" int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
                              void *out,
                              int32_t *dev_status,
                              void *stream) {
-    // ---- shape metadata
-    if (n < 0) return fail(DCCONV_EINVAL, "n (decode rows) must be >= 0, got %lld", (long long)n);
-    if (d < 1) return fail(DCCONV_EINVAL, "d (channels) must be >= 1, got %lld", (long long)d);
-    if (s < 0) return fail(DCCONV_EINVAL, "s (state slots) must be >= 0, got %lld", (long long)s);
-    if (w < 1) return fail(DCCONV_EINVAL, "w (filter width) must be >= 1, got %lld", (long long)w);
-    if (l < w - 1)
-        return fail(DCCONV_EINVAL, "conv_state length l=%lld must be >= w-1=%lld", (long long)l,
-                    (long long)(w - 1));
-    if (ld_x < d)
+    // ---- shape metadata and the served subset
+    dcconv::StateLayout layout;
+    if (n >= 0 && d >= 1 && ld_x < d)
         return fail(DCCONV_EINVAL, "x row stride ld_x=%lld is smaller than d=%lld", (long long)ld_x,
                     (long long)d);
-    if (ld_x > d && ld_x % 8 != 0)
+    if (n >= 0 && d >= 1 && ld_x > d && ld_x % 8 != 0)
         return fail(DCCONV_EINVAL,
                     "padded x rows need ld_x %% 8 == 0 (16-byte aligned rows), got ld_x=%lld for d=%lld",
                     (long long)ld_x, (long long)d);
-    if (activation != DCCONV_ACT_IDENTITY && activation != DCCONV_ACT_SILU)
-        return fail(DCCONV_EINVAL, "activation must be DCCONV_ACT_IDENTITY (0) or DCCONV_ACT_SILU (1), got %d",
-                    activation);
-    if (st_s < 0 || st_d < 0 || st_l < 0)
-        return fail(DCCONV_EINVAL, "conv_state strides must be non-negative");
-
-    // ---- served subset
-    if (cache_seqlens != nullptr)
-        return fail(DCCONV_EUNSUPPORTED,
-                    "cache_seqlens is reserved and must be NULL (circular-buffer state is not served)");
-    if (w != 4) return fail(DCCONV_EUNSUPPORTED, "only filter width w=4 is served, got w=%lld", (long long)w);
-    if (n > kI32Max || d > kI32Max || s > kI32Max || l > 65536)
-        return fail(DCCONV_EUNSUPPORTED, "sizes beyond n, d, s < 2^31 and l <= 65536 are not served");
-    dcconv::StateLayout layout;
-    if (st_l == 1 && st_d == l && (st_s >= d * l || s <= 1)) {
-        layout = dcconv::StateLayout::Compact;
-    } else if (st_d == 1 && st_l == d && (st_s >= l * d || s <= 1)) {
-        layout = dcconv::StateLayout::ChannelLast;
-    } else {
-        return fail(DCCONV_EUNSUPPORTED,
-                    "conv_state strides (%lld, %lld, %lld) are neither compact (>=d*l, l, 1) nor "
-                    "channel-last (>=l*d, 1, d)",
-                    (long long)st_s, (long long)st_d, (long long)st_l);
-    }
-
+    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, cache_seqlens, &layout);
+    if (rc != DCCONV_OK) return rc;
     if (n == 0) return succeed("");
-
-    // ---- pointers
-    if (!x || !weight || !out || (!conv_state && s > 0))
-        return fail(DCCONV_EINVAL, "x, weight, out (and conv_state when s > 0) must be non-NULL when n > 0");
-    if (conv_state_indices == nullptr && s < n)
-        return fail(DCCONV_EINVAL, "without conv_state_indices row r uses slot r, so s=%lld must be >= n=%lld",
-                    (long long)s, (long long)n);
-    if (!aligned(x, 16) || !aligned(conv_state, 16) || !aligned(weight, 16) || !aligned(out, 16) ||
-        (bias && !aligned(bias, 16)))
-        return fail(DCCONV_EINVAL, "BF16 tensors must be 16-byte aligned");
-    if ((conv_state_indices && !aligned(conv_state_indices, 4)) || (dev_status && !aligned(dev_status, 4)))
-        return fail(DCCONV_EINVAL, "conv_state_indices and dev_status must be 4-byte aligned");
-
-    // ---- overlap: nothing the call writes may alias anything else it touches
-    const int64_t state_elems = s > 0 ? (s - 1) * st_s + (d - 1) * st_d + (l - 1) * st_l + 1 : 0;
-    const Span sx = span("x", x, 2 * ((n - 1) * ld_x + d));
-    const Span sst = span("conv_state", conv_state, 2 * state_elems);
-    const Span sw = span("weight", weight, 2 * d * w);
-    const Span sb = span("bias", bias, 2 * d);
-    const Span si = span("conv_state_indices", conv_state_indices, 4 * n);
-    const Span so = span("out", out, 2 * n * d);
-    const Span ss = span("dev_status", dev_status, 4);
-    const Span written[] = {sst, so, ss};
-    const Span all[] = {sx, sst, sw, sb, si, so, ss};
-    for (const Span &a : written)
-        for (const Span &b : all)
-            if (a.name != b.name && overlaps(a, b))
-                return fail(DCCONV_EINVAL, "%s overlaps %s", a.name, b.name);
+    rc = check_pointers(x, 2 * ((n - 1) * ld_x + d), conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias,
+                        conv_state_indices, n, out, 2 * n * d, dev_status);
+    if (rc != DCCONV_OK) return rc;
 
     dcconv::UpdateParams p;
     p.x = static_cast<const uint16_t *>(x);
@@ -161,6 +201,65 @@ extern "C" int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
     const char *name = "";
     const hipError_t err =
         dcconv::launch_update(p, layout, activation, static_cast<hipStream_t>(stream), &name);
+    if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return succeed(name);
+}
+
+extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t t,
+                                    int64_t xs_n, int64_t xs_d, int64_t xs_t,
+                                    void *conv_state, int64_t s, int64_t l,
+                                    int64_t st_s, int64_t st_d, int64_t st_l,
+                                    const void *weight, int64_t w,
+                                    const void *bias,
+                                    const int32_t *conv_state_indices,
+                                    const int32_t *cache_seqlens,
+                                    int activation,
+                                    void *out, int64_t os_n, int64_t os_d, int64_t os_t,
+                                    int32_t *dev_status,
+                                    void *stream) {
+    dcconv::StateLayout layout;
+    if (t < 0) return fail(DCCONV_EINVAL, "t (tokens) must be >= 0, got %lld", (long long)t);
+    if (xs_n < 0 || xs_d < 0 || xs_t < 0 || os_n < 0 || os_d < 0 || os_t < 0)
+        return fail(DCCONV_EINVAL, "x and out strides must be non-negative");
+    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, cache_seqlens, &layout);
+    if (rc != DCCONV_OK) return rc;
+    if (t > kI32Max) return fail(DCCONV_EUNSUPPORTED, "t >= 2^31 tokens is not served");
+    if (n == 0 || t == 0) return succeed("");
+    const int64_t ext[3] = {n, d, t}, ost[3] = {os_n, os_d, os_t};
+    if (!strides_distinct(ext, ost))
+        return fail(DCCONV_EINVAL, "out strides (%lld, %lld, %lld) give two elements the same address",
+                    (long long)os_n, (long long)os_d, (long long)os_t);
+    const int64_t x_bytes = 2 * ((n - 1) * xs_n + (d - 1) * xs_d + (t - 1) * xs_t + 1);
+    const int64_t out_bytes = 2 * ((n - 1) * os_n + (d - 1) * os_d + (t - 1) * os_t + 1);
+    rc = check_pointers(x, x_bytes, conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias, conv_state_indices, n,
+                        out, out_bytes, dev_status);
+    if (rc != DCCONV_OK) return rc;
+
+    dcconv::TokensParams p;
+    p.x = static_cast<const uint16_t *>(x);
+    p.state = static_cast<uint16_t *>(conv_state);
+    p.weight = static_cast<const uint16_t *>(weight);
+    p.bias = static_cast<const uint16_t *>(bias);
+    p.idx = conv_state_indices;
+    p.status = dev_status;
+    p.out = static_cast<uint16_t *>(out);
+    p.xs_n = xs_n;
+    p.xs_d = xs_d;
+    p.xs_t = xs_t;
+    p.os_n = os_n;
+    p.os_d = os_d;
+    p.os_t = os_t;
+    p.st_s = st_s;
+    p.st_d = st_d;
+    p.st_l = st_l;
+    p.n = (int32_t)n;
+    p.d = (int32_t)d;
+    p.t = (int32_t)t;
+    p.s = (int32_t)s;
+    p.l = (int32_t)l;
+    const char *name = "";
+    const hipError_t err =
+        dcconv::launch_update_tokens(p, layout, activation, static_cast<hipStream_t>(stream), &name);
     if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
     return succeed(name);
 }

@@ -39,127 +39,11 @@
 #include <stdint.h>
 
 #include "dcconv.h"
+#include "device_common.h"
 #include "update_params.h"
 
 namespace dcconv {
 namespace {
-
-constexpr int kWave = 64;
-constexpr int kChPerLane = 8;                   // one 16-byte BF16 vector
-constexpr int kChPerWave = kWave * kChPerLane;  // 512 channels
-constexpr int kWavesPerBlock = 2;
-constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kScalarBlock = 256;               // channels per block in the scalar path
-constexpr int64_t kMaxBlocks = 1 << 20;         // grid cap; the kernels stride over units
-// Two rows per wave once the grid still has this many waves: fewer, fuller waves
-// keep more bytes in flight per wave and share one weight load between rows.
-constexpr int64_t kMinWavesForTwoRows = 1024;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Single-use streams: non-temporal 16-byte accesses.
-__device__ __forceinline__ u32x4 load_stream(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-__device__ __forceinline__ void store_stream(void *p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-// Reused data (weights, bias): ordinary cached loads.
-__device__ __forceinline__ u32x4 load_cached(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-// Raw buffer accesses: a descriptor holds a base address and a byte count, and
-// the hardware turns any access at or beyond the count into a zero read or a
-// dropped write.  Word 3 is the gfx9 raw-buffer format (32-bit data format).
-typedef __amdgpu_buffer_rsrc_t Buffer;
-constexpr int kBufferWord3 = 0x00020000;
-constexpr int kCached = 0;  // cache policy: default
-constexpr int kStream = 2;  // cache policy: non-temporal
-__device__ __forceinline__ Buffer make_buffer(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
-}
-template <int POLICY>
-__device__ __forceinline__ u32x4 buffer_load(Buffer b, uint32_t offset) {
-    return __builtin_amdgcn_raw_buffer_load_b128(b, offset, 0, POLICY);
-}
-template <int POLICY>
-__device__ __forceinline__ void buffer_store(u32x4 v, Buffer b, uint32_t offset) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, b, offset, 0, POLICY);
-}
-
-// BF16 held in the low / high half of a 32-bit word, as FP32 (exact).
-__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-// Two FP32 values -> one word holding two BF16 (round to nearest even; gfx950
-// converts a pair in one instruction).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    f32x2_t v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-}
-
-template <int ACT>
-__device__ __forceinline__ float activate(float a);
-template <>
-__device__ __forceinline__ float activate<DCCONV_ACT_IDENTITY>(float a) {
-    return a;
-}
-// SiLU(a) = a / (1 + e^-a), with the hardware base-2 exponential and reciprocal
-// (each within about one FP32 ulp; the result is far inside one BF16 ulp).
-// a -> -inf gives a * rcp(inf) = -0, a -> +inf gives a.
-template <>
-__device__ __forceinline__ float activate<DCCONV_ACT_SILU>(float a) {
-    constexpr float kMinusLog2e = -1.4426950408889634f;
-    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * kMinusLog2e));
-}
-
-// Orders this wave's LDS accesses across lanes.  LDS instructions of one
-// wavefront execute in order, so wavefront-scope fences (which keep the compiler
-// from moving LDS accesses across this point) are all that is needed.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Slot of `row`, or -1 when the row must not touch the state (a padding row, an
-// out-of-range index, or -- when a status word is given -- a slot another row of
-// the batch also selects).  Must be called by all 64 lanes of the wave; the
-// result is wave-uniform.
-__device__ __forceinline__ int route_row(const UpdateParams &p, int row, int lane) {
-    if (p.idx == nullptr) return row;
-    const int slot = p.idx[row];
-    if (slot == -1) return -1;
-    if (slot < -1 || slot >= p.s) {
-        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_INDEX);
-        return -1;
-    }
-    if (p.status != nullptr) {
-        bool hit = false;
-        for (int base = 0; base < p.n; base += kWave) {
-            const int r = base + lane;
-            if (r < p.n && r != row && p.idx[r] == slot) hit = true;
-        }
-        if (__any(hit)) {
-            if (lane == 0) atomicOr(p.status, DCCONV_DEV_DUP_INDEX);
-            return -1;
-        }
-    }
-    return slot;
-}
-
-// 16-bit element e of an array of packed BF16 pairs, as FP32 (e is a constant
-// after unrolling, so this folds to one shift or mask).
-template <int NW>
-__device__ __forceinline__ float elem_f32(const uint32_t (&w)[NW], int e) {
-    return (e & 1) ? hi_f32(w[e >> 1]) : lo_f32(w[e >> 1]);
-}
 
 // The arithmetic for the 8 channels a lane owns.
 //   hist[4L]: the old state of the 8 channels, channel-major (oldest first)
@@ -237,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             const int row = group * R + r;
             // route_row's result is the same in every lane; saying so keeps the
             // buffer descriptors built from it in scalar registers.
-            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p, row, lane) : -2);
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p.idx, p.status, p.n, p.s, row, lane) : -2);
         }
 
         // Issue every load up front: this wave's share of the weight tile, the
@@ -247,12 +131,8 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
         // tile's end fall outside the descriptor.  Nothing below branches on the
         // row, so the compiler can wait for each row's own loads only.
         __builtin_amdgcn_s_setprio(3);  // get the loads of every wave queued early
-        const Buffer wbuf = make_buffer(p.weight + (int64_t)c0 * 4, vec_bytes * 4u);
-        constexpr int kWeightChunks = 4 / kWavesPerBlock;  // 1-KiB pieces of the tile per wave
         u32x4 wraw[kWeightChunks];
-#pragma unroll
-        for (int q = 0; q < kWeightChunks; ++q)
-            wraw[q] = buffer_load<kCached>(wbuf, (uint32_t)((wave * kWeightChunks + q) * 1024) + lane_bytes);
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
         Buffer sbuf[R], obuf[R];
@@ -271,32 +151,9 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
         }
         __builtin_amdgcn_s_setprio(0);
 
-        // Weight tile: 16-byte unit u holds lane u/4's taps for channels
-        // 2(u%4), 2(u%4)+1 of its 8.  It is stored at u ^ ((u >> 4) & 3), which keeps
-        // both the coalesced writes and the per-lane reads (stride 64 bytes) free of
-        // LDS bank conflicts.
-#pragma unroll
-        for (int q = 0; q < kWeightChunks; ++q) {
-            const int u = (wave * kWeightChunks + q) * kWave + lane;
-            weight_tile[u ^ ((u >> 4) & 3)] = wraw[q];
-        }
-        __syncthreads();
         float wf[32], bf[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int u = 4 * lane + k;
-            const u32x4 wk = weight_tile[u ^ ((u >> 4) & 3)];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                wf[8 * k + 2 * q] = lo_f32(wk[q]);
-                wf[8 * k + 2 * q + 1] = hi_f32(wk[q]);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf[2 * q] = lo_f32(bv[q]);
-            bf[2 * q + 1] = hi_f32(bv[q]);
-        }
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
 
         // Finish the rows in order, each once its own loads have landed, and
         // issue every store at the end.  On gfx9 loads and stores share one
@@ -377,16 +234,12 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = group * R + r;
-            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p, row, lane) : -2);
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p.idx, p.status, p.n, p.s, row, lane) : -2);
         }
 
         __builtin_amdgcn_s_setprio(3);
-        const Buffer wbuf = make_buffer(p.weight + (int64_t)c0 * 4, vec_bytes * 4u);
-        constexpr int kWeightChunks = 4 / kWavesPerBlock;
         u32x4 wraw[kWeightChunks];
-#pragma unroll
-        for (int q = 0; q < kWeightChunks; ++q)
-            wraw[q] = buffer_load<kCached>(wbuf, (uint32_t)((wave * kWeightChunks + q) * 1024) + lane_bytes);
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
         Buffer sbuf[R], obuf[R];
@@ -406,28 +259,9 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
         }
         __builtin_amdgcn_s_setprio(0);
 
-#pragma unroll
-        for (int q = 0; q < kWeightChunks; ++q) {
-            const int u = (wave * kWeightChunks + q) * kWave + lane;
-            weight_tile[u ^ ((u >> 4) & 3)] = wraw[q];
-        }
-        __syncthreads();
         float wf[32], bf[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int u = 4 * lane + k;
-            const u32x4 wk = weight_tile[u ^ ((u >> 4) & 3)];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                wf[8 * k + 2 * q] = lo_f32(wk[q]);
-                wf[8 * k + 2 * q + 1] = hi_f32(wk[q]);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf[2 * q] = lo_f32(bv[q]);
-            bf[2 * q + 1] = hi_f32(bv[q]);
-        }
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
 
         // Each plane vector already holds this lane's 8 channels at one history
         // position, so the taps read planes L-3..L-1 directly and the shift is a
@@ -472,7 +306,7 @@ __global__ __launch_bounds__(kScalarBlock) void update_scalar(UpdateParams p, in
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int row = (int)(unit / tiles_per_row);
         const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
-        const int slot = route_row(p, row, lane);
+        const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
         if (c >= p.d) continue;
         uint16_t *o = p.out + (int64_t)row * p.d + c;
         if (slot < 0) {

@@ -23,9 +23,28 @@ struct UpdateParams {
 
 enum class StateLayout { Compact, ChannelLast };
 
+// A multi-token update: T successive decode steps, x and out [n, d, t] at element
+// strides (n, channel, token).  Validated on the host.
+struct TokensParams {
+    const uint16_t *x;
+    uint16_t *state;
+    const uint16_t *weight;
+    const uint16_t *bias;
+    const int32_t *idx;
+    int32_t *status;
+    uint16_t *out;
+    int64_t xs_n, xs_d, xs_t;
+    int64_t os_n, os_d, os_t;
+    int64_t st_s, st_d, st_l;
+    int32_t n, d, t, s, l;
+};
+
 // Picks the specialisation, launches it on `stream` and stores its name in
 // *kernel_name.  Returns hipSuccess or the launch error.
 hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation,
                          hipStream_t stream, const char **kernel_name);
+
+hipError_t launch_update_tokens(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
+                                const char **kernel_name);
 
 }  // namespace dcconv

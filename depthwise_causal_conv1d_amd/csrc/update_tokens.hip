@@ -1,0 +1,311 @@
+// Multi-token decode update for gfx950: T successive decode steps on the same
+// slots in one call, x[N, D, T] -> out[N, D, T].
+//
+// This is the multi-token form the cuDNN FE-OSS page "Causal Conv1d Decode
+// Update" reserves (section "Semantic tensor contract": a future x[N, D, Tstep]
+// keeps the meaning of the state and the weights).  Token t of every row is
+// applied, in order, by the single-step rule, and out[:, :, t] is that step's
+// output.  Doing all T steps in one pass reads and writes each selected state
+// once instead of T times: per active channel-row the bytes drop from
+// T * (4 + 4L) + 2T to 4L + 4T (compact layout).
+//
+//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST>: one wavefront owns one row of one
+//    512-channel tile (8 channels per lane), the block shares the tile's weights.
+//    The history lives in registers in plane-major form (one 16-byte vector per
+//    history position, 8 channels each), so a token's shift is a renaming of
+//    registers.  Tokens go in passes of 8: the pass's x vectors are all loaded
+//    before the first is used and its 8 outputs are all stored after the last
+//    is computed.  Compact state goes through the same LDS stage as the
+//    single-token kernel; channel-last state is already plane-major.
+//  * tokens_scalar<ACT>: one thread per (row, channel), any strides, any L >= 3;
+//    each token is one single-step update of the thread's channel in memory.
+#include <stdint.h>
+
+#include "dcconv.h"
+#include "device_common.h"
+#include "update_params.h"
+
+namespace dcconv {
+namespace {
+
+constexpr int kTokensPerPass = 8;
+// Buffer offsets that lie beyond every descriptor (all descriptors used here are
+// smaller than 2^30 bytes): one for a token past the end, one for a lane past a
+// ragged tile.  Their sum stays below 2^32.
+constexpr uint32_t kBadToken = 1u << 30;
+constexpr uint32_t kBadLane = 1u << 31;
+
+// Two 16-bit halves -> one word: the half `half_lo` of `lo_src` becomes the low
+// half, the half `half_hi` of `hi_src` the high half (one v_perm_b32).
+__device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, int half_lo, uint32_t hi_src, int half_hi) {
+    const uint32_t sel_lo = half_lo ? 0x0302u : 0x0100u;  // bytes of the second operand
+    const uint32_t sel_hi = half_hi ? 0x0706u : 0x0504u;  // bytes of the first operand
+    return __builtin_amdgcn_perm(hi_src, lo_src, (sel_hi << 16) | sel_lo);
+}
+
+__device__ __forceinline__ float half_f32(uint32_t w, int half) { return half ? hi_f32(w) : lo_f32(w); }
+
+// Channel-major words (channel c, position k at element c*L + k) -> planes
+// (plane k, word q holds channels 2q, 2q+1 at position k), and back.
+template <int L>
+__device__ __forceinline__ void to_planes(const uint32_t (&h)[4 * L], u32x4 (&pl)[L]) {
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e_lo = (2 * q) * L + k, e_hi = (2 * q + 1) * L + k;
+            pl[k][q] = pick_halves(h[e_lo >> 1], e_lo & 1, h[e_hi >> 1], e_hi & 1);
+        }
+}
+template <int L>
+__device__ __forceinline__ void from_planes(const u32x4 (&pl)[L], uint32_t (&h)[4 * L]) {
+#pragma unroll
+    for (int i = 0; i < 4 * L; ++i) {
+        const int e0 = 2 * i, e1 = 2 * i + 1;
+        const int c0 = e0 / L, k0 = e0 % L, c1 = e1 / L, k1 = e1 % L;
+        h[i] = pick_halves(pl[k0][c0 >> 1], c0 & 1, pl[k1][c1 >> 1], c1 & 1);
+    }
+}
+
+template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST>
+__global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_per_row, int64_t block_units) {
+    __shared__ u32x4 stage_all[kWavesPerBlock][CHANNEL_LAST ? 1 : kWave * L];
+    __shared__ u32x4 weight_tile[4 * kWave];
+    // Positions read in the channel-last layout: the first token's taps need
+    // L-3..L-1 and the shift needs 1..L-1; position 0 only when it is a tap.
+    constexpr int kFirst = (CHANNEL_LAST && L > 3) ? 1 : 0;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
+
+    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+        const int tile = (int)(bu % tiles_per_row);
+        const int row_raw = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
+        const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+        const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
+        const int slot = __builtin_amdgcn_readfirstlane(row_raw < p.n ? route_row(p.idx, p.status, p.n, p.s, row_raw, lane)
+                                                                       : -2);
+        const bool live = slot >= 0;
+        const int row = min(row_raw, p.n - 1);
+
+        __builtin_amdgcn_s_setprio(3);
+        u32x4 wraw[kWeightChunks];
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        // State: compact = the tile's contiguous run of L KiB, read coalesced;
+        // channel-last = planes kFirst..L-1 of this tile.
+        Buffer sbuf;
+        u32x4 sv[L];
+        if (CHANNEL_LAST) {
+            sbuf = make_buffer(live ? p.state + (int64_t)slot * p.st_s + c0 : p.x,
+                               live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+#pragma unroll
+            for (int k = kFirst; k < L; ++k) sv[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)k + lane_off);
+        } else {
+            sbuf = make_buffer(live ? p.state + (int64_t)slot * p.st_s + (int64_t)c0 * L : p.x,
+                               live ? vec_bytes * L : 0u);
+#pragma unroll
+            for (int j = 0; j < L; ++j) sv[j] = buffer_load<kStream>(sbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
+        }
+        // x and out of this row: one descriptor each, spanning every token.
+        const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.xs_n + c0,
+                                        live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+        const Buffer obuf = make_buffer(p.out + (int64_t)row * p.os_n + c0,
+                                        row_raw < p.n ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+        u32x4 xv[kTokensPerPass];
+#pragma unroll
+        for (int i = 0; i < kTokensPerPass; ++i)
+            xv[i] = buffer_load<kStream>(xbuf, (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
+        __builtin_amdgcn_s_setprio(0);
+
+        float wf[32], bf[8];
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
+
+        u32x4 pl[L];
+        if (CHANNEL_LAST) {
+#pragma unroll
+            for (int k = 0; k < L; ++k) pl[k] = k < kFirst ? u32x4{0u, 0u, 0u, 0u} : sv[k];
+        } else {
+            u32x4 *stage = stage_all[wave];
+#pragma unroll
+            for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[j];
+            wave_lds_sync();
+            uint32_t h[4 * L];
+#pragma unroll
+            for (int k = 0; k < L; ++k) {
+                const u32x4 t = stage[lane * L + k];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) h[4 * k + q] = t[q];
+            }
+            to_planes<L>(h, pl);
+        }
+
+        for (int t0 = 0; t0 < p.t; t0 += kTokensPerPass) {
+            if (t0 > 0) {
+#pragma unroll
+                for (int i = 0; i < kTokensPerPass; ++i)
+                    xv[i] = buffer_load<kStream>(xbuf, (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+            }
+            const int tokens = min(kTokensPerPass, p.t - t0);
+            u32x4 ov[kTokensPerPass];
+#pragma unroll
+            for (int i = 0; i < kTokensPerPass; ++i) {
+                ov[i] = u32x4{0u, 0u, 0u, 0u};
+                if (i < tokens) {
+                    float y[kChPerLane];
+#pragma unroll
+                    for (int ch = 0; ch < kChPerLane; ++ch) {
+                        const int q = ch >> 1, hh = ch & 1;
+                        // history[L+1-W+j] for W = 4: positions L-3..L-1, then x;
+                        // exact BF16 products, j ascending, bias last.
+                        float acc = half_f32(pl[L - 3][q], hh) * wf[4 * ch + 0];
+                        acc = __builtin_fmaf(half_f32(pl[L - 2][q], hh), wf[4 * ch + 1], acc);
+                        acc = __builtin_fmaf(half_f32(pl[L - 1][q], hh), wf[4 * ch + 2], acc);
+                        acc = __builtin_fmaf(half_f32(xv[i][q], hh), wf[4 * ch + 3], acc);
+                        if (HAS_BIAS) acc += bf[ch];
+                        y[ch] = activate<ACT>(acc);
+                    }
+                    if (live)  // a padding row writes zeros
+                        ov[i] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                                      pack_bf16x2(y[6], y[7])};
+                    // the shift: every position moves one place older, x is the newest
+#pragma unroll
+                    for (int k = 0; k < L - 1; ++k) pl[k] = pl[k + 1];
+                    pl[L - 1] = xv[i];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kTokensPerPass; ++i)
+                buffer_store<kStream>(ov[i], obuf, (t0 + i < p.t ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+        }
+
+        // Write the final history back.
+        if (CHANNEL_LAST) {
+#pragma unroll
+            for (int k = 0; k < L; ++k) buffer_store<kStream>(pl[k], sbuf, plane_bytes * (uint32_t)k + lane_off);
+        } else {
+            u32x4 *stage = stage_all[wave];
+            uint32_t h[4 * L];
+            from_planes<L>(pl, h);
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < L; ++k) stage[lane * L + k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+            wave_lds_sync();
+            u32x4 nv[L];
+#pragma unroll
+            for (int j = 0; j < L; ++j) nv[j] = stage[j * kWave + lane];
+#pragma unroll
+            for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[j], sbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
+        }
+        __syncthreads();  // the stage and the weight tile are reused by the next unit
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kScalarBlock) void tokens_scalar(TokensParams p, int tiles_per_row, int64_t units) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int row = (int)(unit / tiles_per_row);
+        const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
+        const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
+        if (c >= p.d) continue;
+        uint16_t *o = p.out + (int64_t)row * p.os_n + (int64_t)c * p.os_d;
+        if (slot < 0) {
+            for (int t = 0; t < p.t; ++t) o[(int64_t)t * p.os_t] = 0;
+            continue;
+        }
+        const int L = p.l;
+        uint16_t *h = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
+        const int64_t sl = p.st_l;
+        const uint16_t *xc = p.x + (int64_t)row * p.xs_n + (int64_t)c * p.xs_d;
+        const uint16_t *wt = p.weight + (int64_t)c * 4;
+        const float w0 = bf16_bits_to_f32(wt[0]), w1 = bf16_bits_to_f32(wt[1]);
+        const float w2 = bf16_bits_to_f32(wt[2]), w3 = bf16_bits_to_f32(wt[3]);
+        const float b = p.bias != nullptr ? bf16_bits_to_f32(p.bias[c]) : 0.0f;
+        for (int t = 0; t < p.t; ++t) {
+            const uint32_t x = xc[(int64_t)t * p.xs_t];
+            const float h0 = bf16_bits_to_f32(h[(L - 3) * sl]);
+            const float h1 = bf16_bits_to_f32(h[(L - 2) * sl]);
+            const float h2 = bf16_bits_to_f32(h[(L - 1) * sl]);
+            for (int k = 0; k < L - 1; ++k) h[k * sl] = h[(k + 1) * sl];
+            h[(L - 1) * sl] = (uint16_t)x;
+            float acc = h0 * w0;
+            acc = __builtin_fmaf(h1, w1, acc);
+            acc = __builtin_fmaf(h2, w2, acc);
+            acc = __builtin_fmaf(bf16_bits_to_f32(x), w3, acc);
+            if (p.bias != nullptr) acc += b;
+            o[(int64_t)t * p.os_t] = f32_to_bf16_bits(activate<ACT>(acc));
+        }
+    }
+}
+
+template <typename Kernel>
+hipError_t launch_tokens(Kernel kernel, const TokensParams &p, int tiles_per_row, int64_t units, int block,
+                         hipStream_t stream) {
+    int64_t blocks = units < kMaxBlocks ? units : kMaxBlocks;
+    TokensParams args_p = p;
+    void *args[] = {&args_p, &tiles_per_row, &units};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(block), args, 0,
+                           stream);
+}
+
+template <int L, int ACT, bool CL>
+hipError_t launch_tokens_l(const TokensParams &p, int tiles, hipStream_t stream) {
+    const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
+    return p.bias != nullptr ? launch_tokens(tokens_v8<L, ACT, true, CL>, p, tiles, block_units, kBlock, stream)
+                             : launch_tokens(tokens_v8<L, ACT, false, CL>, p, tiles, block_units, kBlock, stream);
+}
+
+template <int ACT, bool CL>
+hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream, const char **name) {
+#define DCCONV_TOK_CASE(LL)                                                                                          \
+    case LL:                                                                                                         \
+        *name = CL ? (ACT ? "tokens_v8<L=" #LL ",silu,channel_last>" : "tokens_v8<L=" #LL ",identity,channel_last>") \
+                   : (ACT ? "tokens_v8<L=" #LL ",silu,compact>" : "tokens_v8<L=" #LL ",identity,compact>");          \
+        return launch_tokens_l<LL, ACT, CL>(p, tiles, stream);
+    switch (p.l) {
+        DCCONV_TOK_CASE(3)
+        DCCONV_TOK_CASE(4)
+        DCCONV_TOK_CASE(5)
+        DCCONV_TOK_CASE(6)
+        DCCONV_TOK_CASE(7)
+        DCCONV_TOK_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef DCCONV_TOK_CASE
+}
+
+}  // namespace
+
+hipError_t launch_update_tokens(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
+                                const char **kernel_name) {
+    const bool silu = activation == DCCONV_ACT_SILU;
+    const int64_t lim = (int64_t)1 << 30;
+    // The vector path needs 16-byte channel vectors everywhere and every buffer
+    // descriptor below 2^30 bytes (see kBadToken / kBadLane).
+    const bool v8 = p.d % kChPerLane == 0 && p.xs_d == 1 && p.os_d == 1 && (p.n == 1 || p.xs_n % 8 == 0) &&
+                    (p.n == 1 || p.os_n % 8 == 0) && (p.t == 1 || (p.xs_t % 8 == 0 && p.os_t % 8 == 0)) &&
+                    p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8 && p.xs_t * 2 * (int64_t)(p.t - 1) + 2 * kChPerWave < lim &&
+                    p.os_t * 2 * (int64_t)(p.t - 1) + 2 * kChPerWave < lim && p.st_l * 2 * (int64_t)p.l + 2 * kChPerWave < lim;
+    if (v8) {
+        const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
+        if (layout == StateLayout::ChannelLast)
+            return silu ? launch_tokens_v8<DCCONV_ACT_SILU, true>(p, tiles, stream, kernel_name)
+                        : launch_tokens_v8<DCCONV_ACT_IDENTITY, true>(p, tiles, stream, kernel_name);
+        return silu ? launch_tokens_v8<DCCONV_ACT_SILU, false>(p, tiles, stream, kernel_name)
+                    : launch_tokens_v8<DCCONV_ACT_IDENTITY, false>(p, tiles, stream, kernel_name);
+    }
+    const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
+    *kernel_name = silu ? "tokens_scalar<silu>" : "tokens_scalar<identity>";
+    return silu ? launch_tokens(tokens_scalar<DCCONV_ACT_SILU>, p, tiles, (int64_t)p.n * tiles, kScalarBlock, stream)
+                : launch_tokens(tokens_scalar<DCCONV_ACT_IDENTITY>, p, tiles, (int64_t)p.n * tiles, kScalarBlock,
+                                stream);
+}
+
+}  // namespace dcconv

@@ -129,6 +129,44 @@ int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
                   int32_t *dev_status,
                   void *stream);
 
+/*
+ * dcconv_update_tokens -- T successive decode steps on the same slots, in place.
+ * The multi-token form the page reserves for x[N, D, Tstep] (section "Semantic
+ * tensor contract": the state and weight meanings do not change): token t of
+ * every row is applied, in order t = 0..T-1, by exactly the rule of
+ * dcconv_update, and out[:, :, t] is that step's output.  One call reads and
+ * writes each selected state once instead of T times.
+ *
+ * x           BF16, element (r, c, t) at x[r*xs_n + c*xs_d + t*xs_t]; strides >= 0.
+ * n, d, t     rows, channels, tokens (t == 0 or n == 0: DCCONV_OK, nothing enqueued).
+ * out         BF16, element (r, c, t) at out[r*os_n + c*os_d + t*os_t]; the strides
+ *             must give every element its own address (no two (r, c, t) alias).
+ * conv_state, s, l, st_*, weight, w, bias, conv_state_indices, cache_seqlens,
+ * activation, dev_status, stream: exactly as for dcconv_update (the routing of a
+ * row is the same for all of its tokens; a padding or rejected row writes zeros
+ * for every token and leaves the state untouched).
+ *
+ * Alignment: x, out and the other BF16 pointers 16-byte aligned.  The fast path
+ * additionally needs unit channel strides and row/token strides that are
+ * multiples of 8 elements; other strides are served by a per-element path.
+ * Nothing the call writes may overlap any other operand.
+ *
+ * Returns DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED or DCCONV_EHIP, with the
+ * same meanings as for dcconv_update.
+ */
+int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t t,
+                         int64_t xs_n, int64_t xs_d, int64_t xs_t,
+                         void *conv_state, int64_t s, int64_t l,
+                         int64_t st_s, int64_t st_d, int64_t st_l,
+                         const void *weight, int64_t w,
+                         const void *bias,
+                         const int32_t *conv_state_indices,
+                         const int32_t *cache_seqlens,
+                         int activation,
+                         void *out, int64_t os_n, int64_t os_d, int64_t os_t,
+                         int32_t *dev_status,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

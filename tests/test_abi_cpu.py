@@ -202,3 +202,54 @@ def test_frontend_contract_violations(bad):
         x = torch.zeros(16, 4, dtype=torch.bfloat16).t()
     with pytest.raises(ValueError):
         dc.causal_conv1d_update(x, st, w, None, act, **kw)
+
+
+# ------------------------------------------------------ multi-token entry point
+
+
+def _targs(**over):
+    a = dict(x=X, n=4, d=64, t=3, xs_n=192, xs_d=1, xs_t=64, conv_state=ST, s=4, l=3, st_s=192, st_d=3, st_l=1,
+             weight=WT, w=4, bias=None, conv_state_indices=None, cache_seqlens=None, activation=1,
+             out=OUT, os_n=192, os_d=1, os_t=64, dev_status=None, stream=None)
+    a.update(over)
+    return a
+
+
+TOKEN_DECLINES = [
+    (dict(t=-1), dc.DCCONV_EINVAL, "t (tokens)"),
+    (dict(xs_t=-64), dc.DCCONV_EINVAL, "non-negative"),
+    (dict(os_d=-1), dc.DCCONV_EINVAL, "non-negative"),
+    (dict(os_t=32), dc.DCCONV_EINVAL, "same address"),       # tokens overlap channels
+    (dict(os_n=64), dc.DCCONV_EINVAL, "same address"),       # rows overlap tokens
+    (dict(os_d=0), dc.DCCONV_EINVAL, "same address"),
+    (dict(cache_seqlens=IX), dc.DCCONV_EUNSUPPORTED, "cache_seqlens"),
+    (dict(w=3), dc.DCCONV_EUNSUPPORTED, "w=4"),
+    (dict(l=2, st_d=2, st_s=128), dc.DCCONV_EINVAL, "must be >= w-1"),
+    (dict(x=X + 8), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(out=OUT + 2), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(out=X + 512), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(conv_state=OUT + 256), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(s=3), dc.DCCONV_EINVAL, "must be >= n"),
+    (dict(st_s=192, st_d=1, st_l=2), dc.DCCONV_EUNSUPPORTED, "neither compact"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code,frag", TOKEN_DECLINES, ids=[str(d[0]) for d in TOKEN_DECLINES])
+def test_tokens_host_refusals(over, code, frag):
+    rc = dc.dcconv_update_tokens(**_targs(**over))
+    assert rc == code, (rc, dc.dcconv_last_error())
+    assert frag in dc.dcconv_last_error()
+
+
+@no_gpu
+def test_tokens_zero_tokens_or_rows_enqueue_nothing():
+    assert dc.dcconv_update_tokens(**_targs(t=0, x=None, out=None)) == dc.DCCONV_OK
+    assert dc.dcconv_update_tokens(**_targs(n=0, x=None, out=None)) == dc.DCCONV_OK
+    assert dc.dcconv_last_kernel() == ""
+
+
+def test_tokens_frontend_needs_3d_x():
+    _, st, w = _cpu_args()
+    with pytest.raises(ValueError, match=r"\[N, D, T\]"):
+        dc.causal_conv1d_update_tokens(torch.zeros(4, 16, dtype=torch.bfloat16), st, w)
