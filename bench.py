@@ -36,16 +36,22 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s + decode rows/s, conv1d_update N=256 D=8192 W=4"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "depthwise_causal_conv1d_amd", "csrc", "update.hip")
+CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_amd", "csrc")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a kernel is compiled from (its file and the shared
+    device helpers), so stale counter summaries are recognised."""
+    main = "update_tokens.hip" if kernel.startswith("tokens_") else "update.hip"
+    h = hashlib.sha256()
+    for name in (main, "device_common.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str, workload: str):
@@ -60,7 +66,7 @@ def read_traffic(kernel: str, workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash() or vals.get("kernel") != kernel:
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel) or vals.get("kernel") != kernel:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -83,8 +89,9 @@ class Workload:
         def up(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
-        set_bytes = (data["x"][0].nbytes + data["state"].nbytes + data["weight"].nbytes
-                     + 2 * spec.N * spec.D + (data["bias"].nbytes if data["bias"] is not None else 0))
+        self.tokens = spec.T if spec.one_call else 1
+        set_bytes = (data["x"][0].nbytes * self.tokens + data["state"].nbytes + data["weight"].nbytes
+                     + 2 * spec.N * spec.D * self.tokens + (data["bias"].nbytes if data["bias"] is not None else 0))
         self.n_sets = min(128, max(1, int(math.ceil(rotate_bytes / set_bytes))))
         self.sets = []
         x_all = up(data["x"])  # [T, N, ld]
@@ -99,20 +106,27 @@ class Workload:
                 weight=up(data["weight"]),
                 bias=None if data["bias"] is None else up(data["bias"]),
                 idx=idx,
-                out=torch.empty(spec.N, spec.D, dtype=torch.bfloat16, device=dev)))
+                out=torch.empty(spec.N, self.tokens, spec.D, dtype=torch.bfloat16, device=dev)))
         self.set_bytes = set_bytes
         active = spec.N if data["indices"] is None else int((data["indices"] >= 0).sum())
         self.bytes_per_call = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active,
                                                    data["bias"] is not None, data["indices"] is not None,
-                                                   spec.layout)
+                                                   spec.layout, self.tokens)
 
     def step(self, i: int):
         import depthwise_causal_conv1d_amd as dc
 
         s = self.sets[i % self.n_sets]
+        D = self.spec.D
+        if self.spec.one_call:
+            # x [T, N, ld] seen as [N, D, T]; out [N, T, D] seen as [N, D, T]
+            dc.causal_conv1d_update_tokens(s["x"][:, :, :D].permute(1, 2, 0), s["state"], s["weight"], s["bias"],
+                                           self.spec.act, out=s["out"].permute(0, 2, 1),
+                                           conv_state_indices=s["idx"])
+            return
         t = (i // self.n_sets) % self.spec.T
-        dc.causal_conv1d_update_out(s["x"][t, :, :self.spec.D], s["state"], s["weight"], s["bias"],
-                                    self.spec.act, out=s["out"], conv_state_indices=s["idx"])
+        dc.causal_conv1d_update_out(s["x"][t, :, :D], s["state"], s["weight"], s["bias"],
+                                    self.spec.act, out=s["out"][:, 0, :], conv_state_indices=s["idx"])
 
 
 def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
@@ -153,7 +167,8 @@ def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
     ms = start.elapsed_time(end) / steps
     res = dict(workload=spec.name, kernel=kernel, ms_per_step=ms, us_per_call=ms * 1e3,
                wall_ms_per_step=wall * 1e3 / steps, bytes_per_call=wk.bytes_per_call,
-               gbs=wk.bytes_per_call / (ms * 1e-3) / 1e9, rows_per_s=spec.N / (ms * 1e-3),
+               gbs=wk.bytes_per_call / (ms * 1e-3) / 1e9, rows_per_s=spec.N * wk.tokens / (ms * 1e-3),
+               tokens_per_call=wk.tokens,
                buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
     res["frac"] = res["gbs"] / PEAK_HBM_GBS
     host = wk.host
@@ -168,23 +183,28 @@ def cpu_baseline(spec, host, seconds: float):
     import oracle
     from depthwise_causal_conv1d_amd import workloads as wl
 
-    x = np.ascontiguousarray(host["x"][0])
+    tokens = spec.T if spec.one_call else 1
+    x = np.ascontiguousarray(host["x"][0]) if tokens == 1 else np.ascontiguousarray(host["x"])
     reps, t_total = 0, 0.0
     while reps < 2 or t_total < seconds:
         st = host["state"].copy()
         t0 = time.perf_counter()
-        oracle.update(x, st, host["weight"], host["bias"], spec.act,
-                      conv_state_indices=host["indices"], d=spec.D, ld=spec.ld)
+        if tokens == 1:
+            oracle.update_strided(x, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
+                                  host["weight"], host["bias"], host["indices"], spec.act)
+        else:
+            oracle.update_tokens(x, spec.N, spec.D, tokens, (spec.ld, 1, spec.N * spec.ld), st, spec.S, spec.L,
+                                 wl.state_strides(spec), host["weight"], host["bias"], host["indices"], spec.act)
         t_total += time.perf_counter() - t0
         reps += 1
     active = spec.N if host["indices"] is None else int((host["indices"] >= 0).sum())
     b = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active, host["bias"] is not None,
-                             host["indices"] is not None, spec.layout)
+                             host["indices"] is not None, spec.layout, tokens)
     per_call = t_total / reps
     return {"value": b / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}) on host "
-                      f"arrays, single thread, {per_call * 1e3:.1f} ms per call",
-            "rows_per_s": spec.N / per_call}
+            "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}, {tokens} token(s)) "
+                      f"on host arrays, single thread, {per_call * 1e3:.1f} ms per call",
+            "rows_per_s": spec.N * tokens / per_call}
 
 
 def environment():
@@ -266,9 +286,11 @@ def main():
             r, _ = measure(other, max(200, args.steps // 5), 20, min(args.rotate_mb, 512.0), args.launch)
             log(f"[bench] {other.name}: {r['us_per_call']:.3f} us/call, {r['gbs']:.1f} GB/s, "
                 f"{r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}")
-            others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
-                           if k in ("workload", "kernel", "us_per_call", "gbs", "frac", "rows_per_s",
-                                    "bytes_per_call")})
+            entry = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
+                     if k in ("workload", "kernel", "us_per_call", "gbs", "frac", "rows_per_s",
+                              "bytes_per_call", "tokens_per_call")}
+            entry["traffic"] = read_traffic(r["kernel"], other.name)
+            others.append(entry)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, host, args.cpu_seconds)

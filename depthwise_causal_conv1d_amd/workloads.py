@@ -44,6 +44,7 @@ class Spec:
     weight_dist: str = "normal"   # "normal" N(0,1) or "uniform" U(-0.5, 0.5)
     seed: int = 0
     layout: str = "compact"       # conv_state layout: "compact" [S, D, L] or "channel_last" [S, L, D]
+    one_call: bool = False        # the T tokens go in one multi-token call (x viewed as [N, D, T])
 
 
 # The five synthetic configurations.  Index 0 is the tiny case, 3 is the large
@@ -63,9 +64,17 @@ CONFIGS = [
 # Further workloads the benchmark reports beside the five (not parity configurations):
 # the large decode batch with its state handed over channel-last, as a prefill
 # leaves it.
+#
+# The multi-token form: the long-history workload's 16 steps as one call, and the
+# large decode batch advanced 4 tokens per call (as when several drafted tokens
+# are verified at once).
 EXTRA = [
     Spec("large_decode_channel_last", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
          routing="none", weight_dist="uniform", seed=4, layout="channel_last"),
+    Spec("long_history_one_call", N=128, D=4096, W=4, L=8, S=1024, ld=4096, bias=True, act=None,
+         routing="unique", T=16, seed=5, one_call=True),
+    Spec("large_decode_4tok", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
+         routing="none", T=4, weight_dist="uniform", seed=4, one_call=True),
 ]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
@@ -131,16 +140,18 @@ def state_strides(spec: Spec):
 
 
 def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bool,
-                      indices: bool, layout: str = "compact") -> int:
-    """Bytes one decode call must move at minimum: x and the selected state read,
-    the state written back (the history shifts, so all L values are rewritten),
-    weight, bias, output, index table.  Padding rows read no x and no state.
+                      indices: bool, layout: str = "compact", tokens: int = 1) -> int:
+    """Bytes one call that applies ``tokens`` decode steps must move at minimum:
+    x of every token and the selected state read once, the state written back
+    once (the history shifts, so all L values are rewritten), weight, bias, the
+    output of every token, index table.  Padding rows read no x and no state.
 
     State read: in the compact layout a channel's L values are adjacent, so all L
-    are read.  Channel-last keeps each history position in its own plane, and
-    position 0 is only needed when it is also a tap (L == W - 1 = 3), so
-    max(W - 1, L - 1) positions are read."""
-    A = active_rows
-    read_positions = L if layout == "compact" else max(W - 1, L - 1)
-    return (2 * A * D + 2 * A * D * read_positions + 2 * A * D * L + 2 * D * W
-            + (2 * D if bias else 0) + 2 * N * D + (4 * N if indices else 0))
+    are read.  Channel-last keeps each history position in its own plane; a
+    position is needed if it is a tap of the first token (positions >= L-(W-1))
+    or survives into the final state (positions >= tokens), so
+    L - min(tokens, L - (W-1)) planes are read (max(W-1, L-1) for one token)."""
+    A, T = active_rows, tokens
+    read_positions = L if layout == "compact" else L - min(T, L - (W - 1))
+    return (2 * A * D * T + 2 * A * D * read_positions + 2 * A * D * L + 2 * D * W
+            + (2 * D if bias else 0) + 2 * N * D * T + (4 * N if indices else 0))

@@ -1,0 +1,76 @@
+"""Host-side logic of the benchmark: the algorithmic byte count that the
+roofline fraction divides by, the workload generator's shapes, the single-GPU
+refusal and the CPU-baseline leg (runs the oracle; no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from depthwise_causal_conv1d_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_large_decode_bytes_by_hand():
+    # x 256*8192*2, state read 3 positions and written 3, weight 8192*4*2, out 256*8192*2
+    N, D = 256, 8192
+    hand = 2 * N * D + 2 * N * D * 3 + 2 * N * D * 3 + 2 * D * 4 + 2 * N * D
+    assert hand == 33619968
+    assert wl.algorithmic_bytes(N, D, 4, 3, N, False, False) == hand
+
+
+def test_bytes_count_padding_rows_bias_and_indices():
+    N, D, L = 64, 4096, 3
+    full = wl.algorithmic_bytes(N, D, 4, L, N, False, False)
+    part = wl.algorithmic_bytes(N, D, 4, L, 56, True, True)
+    # 8 padding rows skip x, state read and state write; bias and index table added
+    assert full - part == 8 * (2 * D + 2 * D * L * 2) - 2 * D - 4 * N
+
+
+@pytest.mark.parametrize("L,T,planes", [(3, 1, 3), (3, 7, 3), (4, 1, 3), (8, 1, 7), (8, 3, 5), (8, 5, 3),
+                                        (8, 16, 3)])
+def test_channel_last_reads_only_needed_planes(L, T, planes):
+    N, D = 2, 64
+    b = wl.algorithmic_bytes(N, D, 4, L, N, False, False, "channel_last", T)
+    assert b == 2 * N * D * T + 2 * N * D * planes + 2 * N * D * L + 2 * D * 4 + 2 * N * D * T
+
+
+def test_tokens_scale_x_and_out_but_not_state():
+    N, D, L = 128, 4096, 8
+    one = wl.algorithmic_bytes(N, D, 4, L, N, True, True, "compact", 1)
+    sixteen = wl.algorithmic_bytes(N, D, 4, L, N, True, True, "compact", 16)
+    assert sixteen - one == 15 * (2 * N * D + 2 * N * D)
+
+
+def test_workload_shapes_and_padding():
+    for spec in wl.CONFIGS + wl.EXTRA:
+        if spec.N * spec.D * spec.T > 4_000_000:
+            continue
+        d = wl.make(spec)
+        assert d["x"].shape == (spec.T, spec.N, spec.ld)
+        assert np.all(d["x"][:, :, spec.D:] == wl.PAD_SENTINEL)
+        assert d["weight"].shape == (spec.D, spec.W)
+        shape = (spec.S, spec.D, spec.L) if spec.layout == "compact" else (spec.S, spec.L, spec.D)
+        assert d["state"].shape == shape
+        if d["indices"] is not None:
+            real = d["indices"][d["indices"] >= 0]
+            assert len(set(real.tolist())) == len(real) and real.max() < spec.S
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name", ["tiny", "long_history_one_call"])
+def test_cpu_baseline_leg(name):
+    spec = wl.BY_NAME[name]
+    res = bench.cpu_baseline(spec, wl.make(spec), seconds=0.0)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "GB/s" and res["value"] > 0
+    json.dumps(res)
