@@ -6,7 +6,9 @@ check and the benchmark's CPU-baseline leg may import this module; the GPU
 library never calls it and shares no code with it.
 
 Semantics follow the cuDNN FE-OSS page "Causal Conv1d Decode Update",
-sections "Causal Conv1d Decode Update" and "Semantic tensor contract".
+sections "Causal Conv1d Decode Update" and "Semantic tensor contract"; the
+prefill (``prefill``) is the full-sequence convolution that page names at its
+top, read as the convolution whose final state the decode update continues.
 """
 from __future__ import annotations
 
@@ -64,6 +66,12 @@ def lib() -> ctypes.CDLL:
                                                vp, i64, i64, i64, i64, i64,        # state, s, l, st_s, st_d, st_l
                                                vp, i64, vp, vp, i32,               # weight, w, bias, indices, act
                                                vp, vp, i64, i64, i64]              # out, out_f32, os_n, os_d, os_t
+            L.oracle_prefill.restype = i32
+            L.oracle_prefill.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp,   # x, n, d, t, xs_n, xs_d, xs_t, starts
+                                         vp, i64, i64, i64, i64, i64,            # state, s, l, st_s, st_d, st_l
+                                         vp, vp,                                 # indices, has_init
+                                         vp, i64, vp, i32,                       # weight, w, bias, act
+                                         vp, vp, i64, i64, i64]                  # out, out_f32, os_n, os_d, os_t
             L.oracle_bf16_to_f32.restype = ctypes.c_float
             L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
             L.oracle_f32_to_bf16.restype = ctypes.c_uint16
@@ -167,6 +175,40 @@ def update_tokens(x_buf, n, d, t, x_strides, state_buf, S, L, state_strides, wei
                                     _ptr(state_buf), S, L, state_strides[0], state_strides[1], state_strides[2],
                                     _ptr(weight), W, _ptr(bias), _ptr(indices), ACT[activation],
                                     _ptr(out), _ptr(out_f32), t * d, 1, d)
+    if rc != OK:
+        raise OracleError(rc)
+    return (out, out_f32) if want_f32 else out
+
+
+def prefill(x_buf, n, d, t, x_strides, weight, bias=None, activation=None, *, starts=None, state_buf=None, S=0,
+            L=0, state_strides=(0, 0, 0), indices=None, has_init=None, want_f32=False):
+    """Full-sequence causal convolution (prefill) over n sequences.
+
+    Batch form (``starts`` None): n sequences of t tokens, token j of sequence i
+    at x_buf[i*xs_n + c*xs_d + j*xs_t]; out is returned as uint16 [n, t, d].
+    Varlen form (``starts`` int32 [n+1]): sequence i is packed tokens
+    starts[i]..starts[i+1]-1 at x_buf[c*xs_d + p*xs_t]; out is [t, d] (packed).
+    ``state_buf`` (None = stateless) holds [S, D, L] at ``state_strides`` and
+    receives the final states in place; ``has_init`` uint8 [n] or None (zeros).
+    """
+    _need(x_buf, np.uint16, "x_buf"); _need(weight, np.uint16, "weight")
+    if state_buf is not None:
+        _need(state_buf, np.uint16, "state_buf")
+    if starts is not None:
+        _need(starts, np.int32, "starts")
+    if has_init is not None:
+        _need(has_init, np.uint8, "has_init")
+    W = weight.shape[1]
+    if starts is None:
+        shape, os_ = (n, t, d), (t * d, 1, d)
+    else:
+        shape, os_ = (t, d), (0, 1, d)
+    out = np.zeros(shape, dtype=np.uint16)
+    out_f32 = np.zeros(shape, dtype=np.float32) if want_f32 else None
+    rc = lib().oracle_prefill(_ptr(x_buf), n, d, t, x_strides[0], x_strides[1], x_strides[2], _ptr(starts),
+                              _ptr(state_buf), S, L, state_strides[0], state_strides[1], state_strides[2],
+                              _ptr(indices), _ptr(has_init), _ptr(weight), W, _ptr(bias), ACT[activation],
+                              _ptr(out), _ptr(out_f32), os_[0], os_[1], os_[2])
     if rc != OK:
         raise OracleError(rc)
     return (out, out_f32) if want_f32 else out

@@ -9,7 +9,10 @@
  * Source of the semantics: the cuDNN FE-OSS page "Causal Conv1d Decode Update"
  * (docs.nvidia.com/cudnn/latest/fe-oss-apis/causal_conv1d_update), sections
  * "Causal Conv1d Decode Update" (the update rule, bias default, activations,
- * slot routing and padding rows) and "Semantic tensor contract" (shapes, strides).
+ * slot routing and padding rows) and "Semantic tensor contract" (shapes, strides,
+ * the reserved multi-token form).  The full-sequence prefill (oracle_prefill) is
+ * the operation that page names at its top for whole sequences; its own page is
+ * not among the sources, and the reading taken is stated above the function.
  *
  * Arithmetic: FP32, one rounding to BF16 at the end, as the accuracy contract of
  * this library fixes ("FP32-accumulated oracle rounded once").  The page itself
@@ -229,6 +232,128 @@ int oracle_update_tokens(const uint16_t *x, int64_t n_rows, int64_t d, int64_t t
                         os_n, os_d, hist, hist_bits);
     }
     free(slot_of_row); free(hist); free(hist_bits);
+    return rc;
+}
+
+/*
+ * Full-sequence causal convolution (prefill), the operation the page names
+ * cudnn.ops.causal_conv1d at its top: it produces the final state that the
+ * decode update then continues.  The prefill page itself is not among the
+ * sources, so this follows the plainest reading that the decode page supports:
+ * a sequence of tokens x_0..x_{T-1} convolved causally over its history, which
+ * is the initial state (or zeros), with the final state the newest L values of
+ * that history.  For one channel c of sequence i:
+ *
+ *   ext          = concat(init[0:L], x[i, c, 0:T])           (L + T values)
+ *   out[i, c, j] = act(sum_k ext[L + j - (w-1) + k] * weight[c, k] + bias[c])
+ *   final[0:L]   = ext[T : T + L]                             (the newest L)
+ *
+ * with the sum in FP32, k ascending from zero, the bias last, one BF16 rounding;
+ * init is the slot's state when has_init[i] is nonzero, else zeros.
+ *
+ *   starts   NULL: n sequences of t tokens each, token j of sequence i at
+ *            x[i*xs_n + c*xs_d + j*xs_t] (out likewise with os_*).
+ *            Else int32 [n+1] with 0 = starts[0] <= ... <= starts[n] = t:
+ *            sequence i is packed tokens starts[i] .. starts[i+1]-1, token j at
+ *            x[c*xs_d + (starts[i] + j)*xs_t]; xs_n and os_n are not used.
+ *   state    NULL: no initial and no final state (history starts at zero, L is
+ *            taken as w-1).  Else [s_slots, d, l] at strides (st_s, st_d, st_l);
+ *            sequence i uses slot indices[i] (or i), -1 = padding: its outputs
+ *            are zero and it touches no slot.  The final state replaces the slot.
+ *   has_init NULL (every sequence starts from zeros) or uint8 [n].
+ * Returns ORACLE_OK, or an error code before mutating anything.
+ */
+int oracle_prefill(const uint16_t *x, int64_t n_seqs, int64_t d, int64_t t,
+                   int64_t xs_n, int64_t xs_d, int64_t xs_t, const int32_t *starts,
+                   uint16_t *state, int64_t s_slots, int64_t l,
+                   int64_t st_s, int64_t st_d, int64_t st_l,
+                   const int32_t *indices, const uint8_t *has_init,
+                   const uint16_t *weight, int64_t w, const uint16_t *bias, int activation,
+                   uint16_t *out, float *out_f32, int64_t os_n, int64_t os_d, int64_t os_t)
+{
+    if (n_seqs < 0 || d < 1 || t < 0 || w < 1)
+        return ORACLE_EARGS;
+    if (activation != ORACLE_ACT_IDENTITY && activation != ORACLE_ACT_SILU)
+        return ORACLE_EARGS;
+    if (state == NULL) {
+        if (indices || has_init)
+            return ORACLE_EARGS;
+        l = w - 1;
+        s_slots = 0;
+    } else if (l < w - 1 || l < 1 || s_slots < 0 || (!indices && s_slots < n_seqs)) {
+        return ORACLE_EARGS;
+    }
+    if (starts) {
+        if (starts[0] != 0 || starts[n_seqs] != t)
+            return ORACLE_EARGS;
+        for (int64_t i = 0; i < n_seqs; ++i)
+            if (starts[i + 1] < starts[i])
+                return ORACLE_EARGS;
+    }
+    if (n_seqs == 0)
+        return ORACLE_OK;
+    if (!weight || (t > 0 && (!x || !out)))
+        return ORACLE_EARGS;
+
+    int64_t *slot_of_seq = (int64_t *)malloc((size_t)n_seqs * sizeof(int64_t));
+    if (!slot_of_seq)
+        return ORACLE_EARGS;
+    int rc = ORACLE_OK;
+    if (state)
+        rc = resolve_slots(indices, n_seqs, s_slots, slot_of_seq);
+    else
+        for (int64_t i = 0; i < n_seqs; ++i)
+            slot_of_seq[i] = i;   /* every sequence live, no slot behind it */
+    int64_t max_len = 0;
+    for (int64_t i = 0; i < n_seqs; ++i) {
+        int64_t len = starts ? (int64_t)starts[i + 1] - starts[i] : t;
+        if (len > max_len)
+            max_len = len;
+    }
+    uint16_t *ext = (uint16_t *)malloc((size_t)(l + max_len) * sizeof(uint16_t));
+    if (!ext)
+        rc = ORACLE_EARGS;
+    for (int64_t i = 0; rc == ORACLE_OK && i < n_seqs; ++i) {
+        int64_t len = starts ? (int64_t)starts[i + 1] - starts[i] : t;
+        const uint16_t *xi = starts ? x + (int64_t)starts[i] * xs_t : x + i * xs_n;
+        uint16_t *oi = starts ? out + (int64_t)starts[i] * os_t : out + i * os_n;
+        float *fi = out_f32 ? (starts ? out_f32 + (int64_t)starts[i] * os_t : out_f32 + i * os_n) : NULL;
+        int64_t slot = slot_of_seq[i];
+        if (slot == -1) {                     /* padding sequence: zero outputs only */
+            for (int64_t c = 0; c < d; ++c)
+                for (int64_t j = 0; j < len; ++j) {
+                    oi[c * os_d + j * os_t] = 0;
+                    if (fi)
+                        fi[c * os_d + j * os_t] = 0.0f;
+                }
+            continue;
+        }
+        int from_state = state != NULL && has_init != NULL && has_init[i] != 0;
+        for (int64_t c = 0; c < d; ++c) {
+            uint16_t *sc = state ? state + slot * st_s + c * st_d : NULL;
+            for (int64_t k = 0; k < l; ++k)
+                ext[k] = from_state ? sc[k * st_l] : (uint16_t)0;
+            for (int64_t j = 0; j < len; ++j)
+                ext[l + j] = xi[c * xs_d + j * xs_t];
+            for (int64_t j = 0; j < len; ++j) {
+                float acc = 0.0f;
+                for (int64_t k = 0; k < w; ++k)
+                    acc = acc + oracle_bf16_to_f32(ext[l + j - (w - 1) + k]) *
+                                    oracle_bf16_to_f32(weight[c * w + k]);
+                if (bias)
+                    acc = acc + oracle_bf16_to_f32(bias[c]);
+                float y = act_apply(acc, activation);
+                if (fi)
+                    fi[c * os_d + j * os_t] = y;
+                oi[c * os_d + j * os_t] = oracle_f32_to_bf16(y);
+            }
+            if (sc)
+                for (int64_t k = 0; k < l; ++k)
+                    sc[k * st_l] = ext[len + k];
+        }
+    }
+    free(slot_of_seq);
+    free(ext);
     return rc;
 }
 
