@@ -11,7 +11,9 @@ weight, bias, activation``, keyword-only ``cache_seqlens`` and
 ``conv_state_indices``; ``conv_state`` is updated in place and a newly allocated
 output is returned.  ``causal_conv1d_update_out`` writes into a caller buffer and
 allocates nothing.  ``causal_conv1d_update_tokens`` applies T tokens per row in one
-call (the multi-token form x[N, D, T] the page reserves).
+call (the multi-token form x[N, D, T] the page reserves).  ``causal_conv1d`` is the
+full-sequence prefill the page names at its top, returning the final state the
+update continues (batch or packed variable-length sequences).
 
 There is no fallback: if the HIP library is missing, every call raises.
 """
@@ -26,12 +28,13 @@ __all__ = [
     "DCCONV_ACT_IDENTITY", "DCCONV_ACT_SILU", "DCCONV_DEV_BAD_INDEX", "DCCONV_DEV_DUP_INDEX",
     "dcconv_abi_version", "dcconv_last_error", "dcconv_last_kernel", "dcconv_update",
     "dcconv_update_tokens", "causal_conv1d_update", "causal_conv1d_update_out",
-    "causal_conv1d_update_tokens", "library_path", "DcconvError",
+    "causal_conv1d_update_tokens", "dcconv_prefill", "causal_conv1d", "library_path", "DcconvError",
+    "DCCONV_DEV_BAD_SEQ",
 ]
 
 DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED, DCCONV_EHIP = 0, 1, 2, 3
 DCCONV_ACT_IDENTITY, DCCONV_ACT_SILU = 0, 1
-DCCONV_DEV_BAD_INDEX, DCCONV_DEV_DUP_INDEX = 1, 2
+DCCONV_DEV_BAD_INDEX, DCCONV_DEV_DUP_INDEX, DCCONV_DEV_BAD_SEQ = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdcconv.so")
@@ -82,6 +85,15 @@ def _load() -> ctypes.CDLL:
                                                  vp, vp, i32,                # indices, cache_seqlens, activation
                                                  vp, i64, i64, i64,          # out, os_n, os_d, os_t
                                                  vp, vp]                     # dev_status, stream
+            lib.dcconv_prefill.restype = i32
+            lib.dcconv_prefill.argtypes = [vp, i64, i64, i64,                # x, n, d, t
+                                           i64, i64, i64, vp,                # xs_n, xs_d, xs_t, seq_starts
+                                           vp, i64, i64,                     # conv_state, s, l
+                                           i64, i64, i64,                    # st_s, st_d, st_l
+                                           vp, vp,                           # indices, has_initial_state
+                                           vp, i64, vp, i32,                 # weight, w, bias, activation
+                                           vp, i64, i64, i64,                # out, os_n, os_d, os_t
+                                           vp, vp]                           # dev_status, stream
             _lib = lib
     return _lib
 
@@ -128,6 +140,15 @@ def dcconv_update_tokens(x, n, d, t, xs_n, xs_d, xs_t, conv_state, s, l, st_s, s
     return _load().dcconv_update_tokens(x, n, d, t, xs_n, xs_d, xs_t, conv_state, s, l, st_s, st_d, st_l, weight,
                                         w, bias, conv_state_indices, cache_seqlens, activation, out, os_n, os_d,
                                         os_t, dev_status, stream)
+
+
+def dcconv_prefill(x, n, d, t, xs_n, xs_d, xs_t, seq_starts, conv_state, s, l, st_s, st_d, st_l,
+                   conv_state_indices, has_initial_state, weight, w, bias, activation, out, os_n, os_d, os_t,
+                   dev_status, stream) -> int:
+    """The prefill C entry point, one to one (pointers as ints)."""
+    return _load().dcconv_prefill(x, n, d, t, xs_n, xs_d, xs_t, seq_starts, conv_state, s, l, st_s, st_d, st_l,
+                                  conv_state_indices, has_initial_state, weight, w, bias, activation, out, os_n,
+                                  os_d, os_t, dev_status, stream)
 
 
 # ------------------------------------------------------------ tensor front end
@@ -253,3 +274,92 @@ def causal_conv1d_update_tokens(x, conv_state, weight, bias=None, activation=Non
                                   stream)
     _raise_for(rc)
     return out
+
+
+def causal_conv1d(x, weight, bias=None, activation=None, *, conv_state=None, conv_state_indices=None,
+                  has_initial_state=None, seq_starts=None, return_final_state=False, out=None, dev_status=None):
+    """Full-sequence causal convolution (prefill) with its final state.
+
+    x: bf16 [N, D, T] at any strides (token-major storage, i.e. a [N, T, D] buffer
+    seen as [N, D, T], is the fast layout).  With ``seq_starts`` (int32 [n+1] on the
+    device) x is [1, D, total_T] holding n packed sequences.
+    conv_state: optional bf16 [S, D, L], read as the initial state of the sequences
+    that ``has_initial_state`` (bool/uint8 [n]) marks and overwritten with every
+    live sequence's final state; ``conv_state_indices`` routes sequences to slots
+    (-1 = padding) as in the decode update.
+    return_final_state: without ``conv_state``, allocate the channel-last
+    [n, D, W-1] final state the decode update accepts in place, and return
+    ``(out, state)``.  Returns ``out`` [N, D, T] otherwise (by default a view of a
+    token-major [N, T, D] buffer).
+    """
+    import torch
+
+    if x.dim() != 3:
+        raise ValueError(f"x must be [N, D, T], got shape {tuple(x.shape)}")
+    for name, t in (("x", x), ("weight", weight), ("bias", bias), ("conv_state", conv_state)):
+        if t is not None and t.requires_grad:
+            raise NotImplementedError(f"inference only: {name} requires grad (training is not served)")
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if activation not in _ACTIVATIONS:
+        raise ValueError(f"activation must be None, 'identity', 'silu' or 'swish', got {activation!r}")
+    B, D, T = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+    if weight.dim() != 2 or weight.shape[0] != D or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous [D, W] tensor")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != D or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [D] tensor")
+    if seq_starts is not None:
+        if B != 1:
+            raise ValueError("with seq_starts, x must be [1, D, total_T] (packed sequences)")
+        if seq_starts.dtype != torch.int32 or seq_starts.dim() != 1 or not seq_starts.is_contiguous():
+            raise ValueError("seq_starts must be a contiguous int32 [n+1] tensor")
+        n = seq_starts.shape[0] - 1
+        if n < 0:
+            raise ValueError("seq_starts must hold at least one entry")
+    else:
+        n = B
+    if has_initial_state is not None:
+        if has_initial_state.dtype not in (torch.bool, torch.uint8) or has_initial_state.shape != (n,) \
+                or not has_initial_state.is_contiguous():
+            raise ValueError("has_initial_state must be a contiguous bool/uint8 [n] tensor")
+    if conv_state_indices is not None and (conv_state_indices.dtype != torch.int32 or
+                                           conv_state_indices.shape != (n,) or
+                                           not conv_state_indices.is_contiguous()):
+        raise ValueError("conv_state_indices must be a contiguous int32 [n] tensor")
+    for name, t in (("weight", weight), ("bias", bias), ("conv_state", conv_state), ("seq_starts", seq_starts),
+                    ("conv_state_indices", conv_state_indices), ("has_initial_state", has_initial_state)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, x on {dev}")
+    state_out = None
+    if conv_state is None and return_final_state:
+        if has_initial_state is not None or conv_state_indices is not None:
+            raise ValueError("has_initial_state and conv_state_indices need a conv_state")
+        W = weight.shape[1]
+        conv_state = torch.empty(n, max(W - 1, 1), D, dtype=torch.bfloat16, device=dev).permute(0, 2, 1)
+        state_out = conv_state
+    if conv_state is not None and (conv_state.dim() != 3 or conv_state.shape[1] != D):
+        raise ValueError(f"conv_state must be [S, D, L] with D={D}, got {tuple(conv_state.shape)}")
+    if out is None:
+        out = torch.empty(B, T, D, dtype=torch.bfloat16, device=dev).permute(0, 2, 1)
+    elif out.shape != (B, D, T) or out.dtype != torch.bfloat16 or out.device != dev:
+        raise ValueError("out must be a bfloat16 [N, D, T] tensor on x's device")
+    if dev_status is not None and (dev_status.dtype != torch.int32 or dev_status.device != dev):
+        raise ValueError("dev_status must be an int32 tensor on x's device")
+    if conv_state is not None:
+        S, _, L = conv_state.shape
+        st = conv_state.stride()
+    else:
+        S, L, st = 0, 0, (0, 0, 0)
+    xs, os_ = x.stride(), out.stride()
+    hi = None if has_initial_state is None else has_initial_state.view(torch.uint8)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = dcconv_prefill(_ptr(x), n, D, T, xs[0], xs[1], xs[2], _ptr(seq_starts), _ptr(conv_state), S, L,
+                            st[0], st[1], st[2], _ptr(conv_state_indices), _ptr(hi), _ptr(weight), weight.shape[1],
+                            _ptr(bias), _ACTIVATIONS[activation], _ptr(out), os_[0], os_[1], os_[2],
+                            _ptr(dev_status), stream)
+    _raise_for(rc)
+    return (out, state_out) if state_out is not None else out

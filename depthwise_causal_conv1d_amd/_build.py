@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdcconv.so")
-SOURCES = ["abi.hip", "update.hip", "update_tokens.hip"]
+SOURCES = ["abi.hip", "update.hip", "update_tokens.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

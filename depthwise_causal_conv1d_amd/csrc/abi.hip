@@ -88,12 +88,15 @@ int check_state_and_shapes(int64_t n, int64_t d, int64_t s, int64_t l, int64_t s
 }
 
 // Pointers, alignment and overlap, once the byte extent of x and out is known.
+// `extra` lists further read-only operands (prefill's sequence table and
+// initial-state flags); x and out may be NULL only when x_bytes == 0.
 int check_pointers(const void *x, int64_t x_bytes, void *conv_state, int64_t s, int64_t d, int64_t l, int64_t st_s,
                    int64_t st_d, int64_t st_l, const void *weight, int64_t w, const void *bias,
-                   const int32_t *conv_state_indices, int64_t n, void *out, int64_t out_bytes, int32_t *dev_status) {
-    if (!x || !weight || !out || (!conv_state && s > 0))
+                   const int32_t *conv_state_indices, int64_t n, void *out, int64_t out_bytes, int32_t *dev_status,
+                   const Span *extra = nullptr, int n_extra = 0, bool stateless = false) {
+    if ((x_bytes > 0 && (!x || !out)) || !weight || (!conv_state && s > 0))
         return fail(DCCONV_EINVAL, "x, weight, out (and conv_state when s > 0) must be non-NULL when n > 0");
-    if (conv_state_indices == nullptr && s < n)
+    if (!stateless && conv_state_indices == nullptr && s < n)
         return fail(DCCONV_EINVAL, "without conv_state_indices row r uses slot r, so s=%lld must be >= n=%lld",
                     (long long)s, (long long)n);
     if (!aligned(x, 16) || !aligned(conv_state, 16) || !aligned(weight, 16) || !aligned(out, 16) ||
@@ -112,10 +115,13 @@ int check_pointers(const void *x, int64_t x_bytes, void *conv_state, int64_t s, 
     const Span ss = span("dev_status", dev_status, 4);
     const Span written[] = {sst, so, ss};
     const Span all[] = {sx, sst, sw, sb, si, so, ss};
-    for (const Span &a : written)
+    for (const Span &a : written) {
         for (const Span &b : all)
             if (a.name != b.name && overlaps(a, b))
                 return fail(DCCONV_EINVAL, "%s overlaps %s", a.name, b.name);
+        for (int k = 0; k < n_extra; ++k)
+            if (overlaps(a, extra[k])) return fail(DCCONV_EINVAL, "%s overlaps %s", a.name, extra[k].name);
+    }
     return DCCONV_OK;
 }
 
@@ -260,6 +266,86 @@ extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t
     const char *name = "";
     const hipError_t err =
         dcconv::launch_update_tokens(p, layout, activation, static_cast<hipStream_t>(stream), &name);
+    if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return succeed(name);
+}
+
+extern "C" int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
+                              int64_t xs_n, int64_t xs_d, int64_t xs_t,
+                              const int32_t *seq_starts,
+                              void *conv_state, int64_t s, int64_t l,
+                              int64_t st_s, int64_t st_d, int64_t st_l,
+                              const int32_t *conv_state_indices,
+                              const uint8_t *has_initial_state,
+                              const void *weight, int64_t w,
+                              const void *bias,
+                              int activation,
+                              void *out, int64_t os_n, int64_t os_d, int64_t os_t,
+                              int32_t *dev_status,
+                              void *stream) {
+    const bool stateful = conv_state != nullptr;
+    const bool packed = seq_starts != nullptr;
+    if (t < 0) return fail(DCCONV_EINVAL, "t (tokens) must be >= 0, got %lld", (long long)t);
+    if (xs_n < 0 || xs_d < 0 || xs_t < 0 || os_n < 0 || os_d < 0 || os_t < 0)
+        return fail(DCCONV_EINVAL, "x and out strides must be non-negative");
+    if (!stateful) {
+        if (s != 0 || conv_state_indices != nullptr || has_initial_state != nullptr)
+            return fail(DCCONV_EINVAL,
+                        "without conv_state, s must be 0 and conv_state_indices and has_initial_state NULL");
+        // no state: validate the rest against a virtual compact [0, d, w-1] state
+        l = w - 1 > 0 ? w - 1 : 1;
+        st_l = 1;
+        st_d = l;
+        st_s = d * l;
+    }
+    dcconv::StateLayout layout;
+    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, nullptr, &layout);
+    if (rc != DCCONV_OK) return rc;
+    if (t > kI32Max) return fail(DCCONV_EUNSUPPORTED, "t >= 2^31 tokens is not served");
+    if (n == 0) return succeed("");
+    if (packed && !aligned(seq_starts, 4)) return fail(DCCONV_EINVAL, "seq_starts must be 4-byte aligned");
+    if (t == 0 && !stateful) return succeed("");  // nothing to read or write
+    const int64_t rows = packed ? 1 : n;
+    int64_t x_bytes = 0, out_bytes = 0;
+    if (t > 0) {
+        const int64_t ext[3] = {rows, d, t}, ost[3] = {os_n, os_d, os_t};
+        if (!strides_distinct(ext, ost))
+            return fail(DCCONV_EINVAL, "out strides (%lld, %lld, %lld) give two elements the same address",
+                        (long long)os_n, (long long)os_d, (long long)os_t);
+        x_bytes = 2 * ((rows - 1) * xs_n + (d - 1) * xs_d + (t - 1) * xs_t + 1);
+        out_bytes = 2 * ((rows - 1) * os_n + (d - 1) * os_d + (t - 1) * os_t + 1);
+    }
+    const Span extra[] = {span("seq_starts", seq_starts, 4 * (n + 1)), span("has_initial_state", has_initial_state, n)};
+    rc = check_pointers(x, x_bytes, conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias, conv_state_indices, n,
+                        out, out_bytes, dev_status, extra, 2, !stateful);
+    if (rc != DCCONV_OK) return rc;
+
+    dcconv::PrefillParams p;
+    p.x = static_cast<const uint16_t *>(x);
+    p.state = static_cast<uint16_t *>(conv_state);
+    p.weight = static_cast<const uint16_t *>(weight);
+    p.bias = static_cast<const uint16_t *>(bias);
+    p.starts = seq_starts;
+    p.idx = conv_state_indices;
+    p.has_init = has_initial_state;
+    p.status = dev_status;
+    p.out = static_cast<uint16_t *>(out);
+    p.xs_n = packed ? 0 : xs_n;
+    p.xs_d = xs_d;
+    p.xs_t = xs_t;
+    p.os_n = packed ? 0 : os_n;
+    p.os_d = os_d;
+    p.os_t = os_t;
+    p.st_s = st_s;
+    p.st_d = st_d;
+    p.st_l = st_l;
+    p.n = (int32_t)n;
+    p.d = (int32_t)d;
+    p.t = (int32_t)t;
+    p.s = (int32_t)s;
+    p.l = (int32_t)l;
+    const char *name = "";
+    const hipError_t err = dcconv::launch_prefill(p, layout, activation, static_cast<hipStream_t>(stream), &name);
     if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
     return succeed(name);
 }

@@ -166,6 +166,43 @@ __device__ __forceinline__ void weight_tile_share(u32x4 *tile, const u32x4 (&raw
     }
 }
 
+// ---- history planes -----------------------------------------------------------
+// A lane's 8 channels of one history position form a "plane" vector (word q
+// holds channels 2q, 2q+1).  The compact state holds the same values
+// channel-major (channel c, position k at element c*L + k of the lane's run).
+
+// Two 16-bit halves -> one word: the half `half_lo` of `lo_src` becomes the low
+// half, the half `half_hi` of `hi_src` the high half (one v_perm_b32).
+__device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, int half_lo, uint32_t hi_src, int half_hi) {
+    const uint32_t sel_lo = half_lo ? 0x0302u : 0x0100u;  // bytes of the second operand
+    const uint32_t sel_hi = half_hi ? 0x0706u : 0x0504u;  // bytes of the first operand
+    return __builtin_amdgcn_perm(hi_src, lo_src, (sel_hi << 16) | sel_lo);
+}
+
+__device__ __forceinline__ float half_f32(uint32_t w, int half) { return half ? hi_f32(w) : lo_f32(w); }
+
+// Channel-major words (channel c, position k at element c*L + k) -> planes
+// (plane k, word q holds channels 2q, 2q+1 at position k), and back.
+template <int L>
+__device__ __forceinline__ void to_planes(const uint32_t (&h)[4 * L], u32x4 (&pl)[L]) {
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e_lo = (2 * q) * L + k, e_hi = (2 * q + 1) * L + k;
+            pl[k][q] = pick_halves(h[e_lo >> 1], e_lo & 1, h[e_hi >> 1], e_hi & 1);
+        }
+}
+template <int L>
+__device__ __forceinline__ void from_planes(const u32x4 (&pl)[L], uint32_t (&h)[4 * L]) {
+#pragma unroll
+    for (int i = 0; i < 4 * L; ++i) {
+        const int e0 = 2 * i, e1 = 2 * i + 1;
+        const int c0 = e0 / L, k0 = e0 % L, c1 = e1 / L, k1 = e1 % L;
+        h[i] = pick_halves(pl[k0][c0 >> 1], c0 & 1, pl[k1][c1 >> 1], c1 & 1);
+    }
+}
+
 __device__ __forceinline__ void unpack_bias(const u32x4 &bv, float (&bf)[8]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

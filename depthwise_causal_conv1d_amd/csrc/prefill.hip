@@ -1,0 +1,515 @@
+// Full-sequence causal convolution (prefill) for gfx950.
+//
+// The cuDNN FE-OSS page "Causal Conv1d Decode Update" names at its top a
+// full-sequence prefill whose final state the decode update continues.  For
+// sequence i (slot s) and channel c, with init = the slot's L values or zeros:
+//
+//   ext          = concat(init, x[i, c, 0:T])
+//   out[i, c, j] = act(sum_k ext[L + j - 3 + k] * w[c, k] + bias[c])
+//   final state  = ext[T : T + L]
+//
+// Outputs j >= 3 depend on x alone, so they need no ordering at all:
+//  * prefill_chunks_v8<ACT, HAS_BIAS>: one wavefront per (512-channel tile,
+//    chunk of kChunk tokens), 8 channels per lane; the block's two waves take
+//    neighbouring chunks of one tile and share its weights.  A chunk re-reads
+//    the 3 tokens before it (its halo); blocks are mapped so that each XCD
+//    walks a contiguous run of chunks, where the halo is the neighbour's data
+//    and mostly hits that XCD's L2.  Tokens go in passes of 8, double
+//    buffered: the next pass's loads are issued before the current pass is
+//    computed and stored.
+//  * prefill_edges_v8<L, ACT, LAYOUT>: everything that touches a slot -- the
+//    first min(3, T) outputs, which read the initial state, and the final
+//    state, which replaces it -- one wavefront per (sequence, tile), so each
+//    slot is read and written by exactly one wave.
+//  * prefill_scalar<ACT>: one thread per (sequence, channel) walking its
+//    tokens in order; any strides, any L >= 3.
+// The edge and chunk kernels write disjoint outputs and read x only, so their
+// order on the stream does not matter; the edges go first.
+#include <stdint.h>
+
+#include "dcconv.h"
+#include "device_common.h"
+#include "update_params.h"
+
+namespace dcconv {
+namespace {
+
+constexpr int kChunk = 32;  // tokens per wave unit of the chunk kernel
+constexpr int kPass = 8;    // tokens per load pass
+constexpr int kXcds = 8;    // MI355X: workgroups go round-robin over 8 XCDs
+// Buffer offsets beyond every descriptor used here (all are below 2^30 bytes):
+// a token outside the piece, and a lane past a ragged tile.  Their sum and any
+// valid offset plus either stay below 2^32.
+constexpr uint32_t kBadToken = 1u << 30;
+constexpr uint32_t kBadLane = 1u << 31;
+
+enum { kStateless = 0, kCompactState = 1, kChannelLastState = 2 };
+
+// Largest i in [0, n] with starts[i] <= p, or -1 (wave-uniform binary search).
+__device__ __forceinline__ int find_seq(const int32_t *starts, int n, int p) {
+    int lo = 0, hi = n + 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (starts[mid] <= p)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo - 1;
+}
+
+// out = act(w0*h0 + w1*h1 + w2*h2 + w3*xt + b) for the lane's 8 channels, in
+// the oracle's order (taps ascending, bias last); BF16 products are exact.
+template <int ACT>
+__device__ __forceinline__ u32x4 conv8(const u32x4 &h0, const u32x4 &h1, const u32x4 &h2, const u32x4 &xt,
+                                       const float (&wf)[32], const float (&bf)[8]) {
+    float y[kChPerLane];
+#pragma unroll
+    for (int ch = 0; ch < kChPerLane; ++ch) {
+        const int q = ch >> 1, hh = ch & 1;
+        float acc = half_f32(h0[q], hh) * wf[4 * ch + 0];
+        acc = __builtin_fmaf(half_f32(h1[q], hh), wf[4 * ch + 1], acc);
+        acc = __builtin_fmaf(half_f32(h2[q], hh), wf[4 * ch + 2], acc);
+        acc = __builtin_fmaf(half_f32(xt[q], hh), wf[4 * ch + 3], acc);
+        acc += bf[ch];
+        y[ch] = activate<ACT>(acc);
+    }
+    return u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+}
+
+// Outputs j in [max(j0, 3), j1) of sequence i, whose token j (channel c0 + ...)
+// is at xseq[j*xs_t] and output at oseq[j*os_t].
+template <int ACT>
+__device__ __forceinline__ void chunk_piece(const PrefillParams &p, int i, int j0, int j1, const uint16_t *xseq,
+                                            uint16_t *oseq, int c0, uint32_t vec_bytes, uint32_t lane_off, int lane,
+                                            const float (&wf)[32], const float (&bf)[8]) {
+    const bool live = route_row(p.idx, p.status, p.n, p.s, i, lane) >= 0;
+    const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u;
+    const int jb = max(j0 - 3, 0);  // first token read: the halo, clipped at the sequence start
+    const Buffer xbuf = make_buffer(xseq + (int64_t)jb * p.xs_t + c0, live ? x_tok * (uint32_t)(j1 - 1 - jb) + vec_bytes : 0u);
+    const Buffer obuf = make_buffer(oseq + (int64_t)j0 * p.os_t + c0, o_tok * (uint32_t)(j1 - 1 - j0) + vec_bytes);
+    auto xoff = [&](int j) -> uint32_t {
+        return ((j >= jb && j < j1) ? x_tok * (uint32_t)(j - jb) : kBadToken) + lane_off;
+    };
+    // the three tokens before j0 (zero before the sequence start; never used there)
+    u32x4 h0 = buffer_load<kStream>(xbuf, xoff(j0 - 3));
+    u32x4 h1 = buffer_load<kStream>(xbuf, xoff(j0 - 2));
+    u32x4 h2 = buffer_load<kStream>(xbuf, xoff(j0 - 1));
+    u32x4 cur[kPass];
+#pragma unroll
+    for (int k = 0; k < kPass; ++k) cur[k] = buffer_load<kStream>(xbuf, xoff(j0 + k));
+    for (int jj = j0; jj < j1; jj += kPass) {
+        u32x4 nxt[kPass];
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) nxt[k] = buffer_load<kStream>(xbuf, xoff(jj + kPass + k));
+        u32x4 ov[kPass];
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) {
+            const u32x4 y = conv8<ACT>(h0, h1, h2, cur[k], wf, bf);
+            ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};  // a padding sequence writes zeros
+            h0 = h1;
+            h1 = h2;
+            h2 = cur[k];
+        }
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) {
+            const int j = jj + k;
+            buffer_store<kStream>(ov[k], obuf,
+                                  ((j >= 3 && j < j1) ? o_tok * (uint32_t)(j - j0) : kBadToken) + lane_off);
+        }
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) cur[k] = nxt[k];
+    }
+}
+
+template <int ACT, bool HAS_BIAS>
+__global__ __launch_bounds__(kBlock) void prefill_chunks_v8(PrefillParams p, int tiles, int64_t units,
+                                                            int64_t units_per_seq, int64_t n_blocks,
+                                                            int64_t v_blocks) {
+    __shared__ u32x4 weight_tile[4 * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const int64_t per_xcd = v_blocks / kXcds;
+    for (int64_t vb = blockIdx.x; vb < v_blocks; vb += gridDim.x) {
+        // workgroup vb runs on XCD vb % 8: give each XCD a contiguous run of blocks
+        const int64_t v = (vb % kXcds) * per_xcd + vb / kXcds;
+        if (v >= n_blocks) continue;  // block-uniform
+        const int tile = (int)(v % tiles);
+        const int64_t unit = (v / tiles) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
+        const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+        const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
+
+        u32x4 wraw[kWeightChunks];
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
+        float wf[32], bf[8];
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
+
+        if (unit < units) {
+            if (p.starts == nullptr) {
+                // batch form: the unit is chunk c of sequence i
+                const int i = (int)(unit / units_per_seq);
+                const int j0 = (int)(unit % units_per_seq) * kChunk;
+                const int j1 = min(p.t, j0 + kChunk);
+                chunk_piece<ACT>(p, i, j0, j1, p.x + (int64_t)i * p.xs_n, p.out + (int64_t)i * p.os_n, c0, vec_bytes,
+                                 lane_off, lane, wf, bf);
+            } else {
+                // packed form: the unit is packed tokens [q, q1), cut at sequence boundaries
+                int q = (int)unit * kChunk;
+                const int q1 = min(p.t, q + kChunk);
+                int i = find_seq(p.starts, p.n, q);
+                while (q < q1) {  // each pass advances q or i; i is bounded by n
+                    if (i < 0 || i >= p.n) break;
+                    const int a = p.starts[i], e = p.starts[i + 1];
+                    if (e <= q && e >= a) {  // an empty sequence at q
+                        ++i;
+                        continue;
+                    }
+                    if (a < 0 || a > q || e < a || e > p.t) {  // not an ordered table: unspecified, stay in bounds
+                        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
+                        break;
+                    }
+                    const int qe = min(q1, e);
+                    chunk_piece<ACT>(p, i, q - a, qe - a, p.x + (int64_t)a * p.xs_t, p.out + (int64_t)a * p.os_t, c0,
+                                     vec_bytes, lane_off, lane, wf, bf);
+                    q = qe;
+                    ++i;
+                }
+            }
+        }
+        __syncthreads();  // the weight tile is reused by the next block unit
+    }
+}
+
+template <int L, int ACT, int LAYOUT>
+__global__ __launch_bounds__(kBlock) void prefill_edges_v8(PrefillParams p, int tiles, int64_t block_units) {
+    // per wave: the compact state's transposition, then the planes, which the
+    // final state picks at a run-time position
+    __shared__ u32x4 stage_all[kWavesPerBlock][kWave * L];
+    __shared__ u32x4 weight_tile[4 * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
+
+    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+        const int tile = (int)(bu % tiles);
+        const int i_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
+        const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+        const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
+        const bool in_range = i_raw < p.n;
+        const int i = min(i_raw, p.n - 1);
+
+        // the sequence's tokens; a packed table that is not ordered is flagged and
+        // the sequence skipped
+        int a = 0, e = p.t;
+        bool ok = in_range;
+        if (p.starts != nullptr) {
+            a = p.starts[i];
+            e = p.starts[i + 1];
+            const bool ordered = a >= 0 && a <= e && e <= p.t && (i > 0 || a == 0) && (i < p.n - 1 || e == p.t);
+            if (in_range && !ordered && p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
+            ok = ok && ordered;
+        }
+        const int len = ok ? e - a : 0;
+        const int slot = __builtin_amdgcn_readfirstlane(ok ? route_row(p.idx, p.status, p.n, p.s, i, lane) : -2);
+        const bool live = slot >= 0;
+        const bool stateful = LAYOUT != kStateless;
+        const bool from_state = stateful && live && p.has_init != nullptr && p.has_init[i] != 0;
+        const bool writes_state = stateful && live;
+        const uint16_t *xseq = p.starts != nullptr ? p.x + (int64_t)a * p.xs_t : p.x + (int64_t)i * p.xs_n;
+        uint16_t *oseq = p.starts != nullptr ? p.out + (int64_t)a * p.os_t : p.out + (int64_t)i * p.os_n;
+        const int nf = min(len, 3);  // outputs written here
+
+        __builtin_amdgcn_s_setprio(3);
+        u32x4 wraw[kWeightChunks];
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
+        const u32x4 bv = buffer_load<kCached>(make_buffer(p.bias != nullptr ? p.bias + c0 : p.weight,
+                                                          p.bias != nullptr ? vec_bytes : 0u),
+                                              lane_bytes);
+        // initial state (zeros unless this sequence continues from its slot)
+        const int64_t slot_base = (int64_t)(live ? slot : 0) * p.st_s;
+        u32x4 sv[L];
+        if (LAYOUT == kChannelLastState) {
+            const Buffer sbuf = make_buffer(p.state + slot_base + c0, from_state ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+#pragma unroll
+            for (int k = 0; k < L; ++k) sv[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)k + lane_off);
+        } else if (LAYOUT == kCompactState) {
+            const Buffer sbuf = make_buffer(p.state + slot_base + (int64_t)c0 * L, from_state ? vec_bytes * L : 0u);
+#pragma unroll
+            for (int j = 0; j < L; ++j) sv[j] = buffer_load<kStream>(sbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
+        } else {
+#pragma unroll
+            for (int k = 0; k < L; ++k) sv[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+        // tokens 0..2 (the outputs here) and the last min(len, L) tokens (the final state)
+        const Buffer xhead = make_buffer(xseq + c0, live && nf > 0 ? x_tok * (uint32_t)(nf - 1) + vec_bytes : 0u);
+        u32x4 xf[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) xf[j] = buffer_load<kStream>(xhead, (j < nf ? x_tok * (uint32_t)j : kBadToken) + lane_off);
+        const int tail0 = max(len - L, 0);
+        const int ntail = len - tail0;
+        const Buffer xtail = make_buffer(xseq + (int64_t)tail0 * p.xs_t + c0,
+                                         writes_state && ntail > 0 ? x_tok * (uint32_t)(ntail - 1) + vec_bytes : 0u);
+        u32x4 xl[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const int tok = len - L + k;  // token that lands at final position k, if >= 0
+            xl[k] = buffer_load<kStream>(xtail, (tok >= 0 ? x_tok * (uint32_t)(tok - tail0) : kBadToken) + lane_off);
+        }
+        __builtin_amdgcn_s_setprio(0);
+
+        float wf[32], bf[8];
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
+
+        u32x4 pl[L];
+        if (LAYOUT == kCompactState) {
+            u32x4 *stage = stage_all[wave];
+#pragma unroll
+            for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[j];
+            wave_lds_sync();
+            uint32_t h[4 * L];
+#pragma unroll
+            for (int k = 0; k < L; ++k) {
+                const u32x4 t = stage[lane * L + k];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) h[4 * k + q] = t[q];
+            }
+            to_planes<L>(h, pl);
+        } else {
+#pragma unroll
+            for (int k = 0; k < L; ++k) pl[k] = sv[k];
+        }
+
+        // outputs 0..2: ext position L + j - 3 + m is init plane (< L) or token (>= L)
+        u32x4 ov[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            u32x4 hv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int pos = L + j - 3 + m;
+                hv[m] = pos < L ? pl[pos < L ? pos : 0] : xf[pos >= L ? pos - L : 0];
+            }
+            const u32x4 y = conv8<ACT>(hv[0], hv[1], hv[2], hv[3], wf, bf);
+            ov[j] = live ? y : u32x4{0u, 0u, 0u, 0u};
+        }
+        // final state: position k is ext[len + k], a token or (len + k < L) the
+        // initial plane len + k, picked through LDS (a run-time position)
+        u32x4 *stage = stage_all[wave];
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < L; ++k) stage[k * kWave + lane] = pl[k];
+        wave_lds_sync();
+        u32x4 fs[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const int m = len + k < L ? len + k : 0;
+            const u32x4 old = stage[m * kWave + lane];
+            fs[k] = (len + k >= L) ? xl[k] : old;
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        const Buffer obuf = make_buffer(oseq + c0, ok && nf > 0 ? o_tok * (uint32_t)(nf - 1) + vec_bytes : 0u);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) buffer_store<kStream>(ov[j], obuf, (j < nf ? o_tok * (uint32_t)j : kBadToken) + lane_off);
+        if (LAYOUT == kChannelLastState) {
+            const Buffer wbuf = make_buffer(p.state + slot_base + c0, writes_state ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+#pragma unroll
+            for (int k = 0; k < L; ++k) buffer_store<kStream>(fs[k], wbuf, plane_bytes * (uint32_t)k + lane_off);
+        } else if (LAYOUT == kCompactState) {
+            uint32_t h[4 * L];
+            from_planes<L>(fs, h);
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < L; ++k) stage[lane * L + k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+            wave_lds_sync();
+            u32x4 nv[L];
+#pragma unroll
+            for (int j = 0; j < L; ++j) nv[j] = stage[j * kWave + lane];
+            const Buffer wbuf = make_buffer(p.state + slot_base + (int64_t)c0 * L, writes_state ? vec_bytes * L : 0u);
+#pragma unroll
+            for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[j], wbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
+        }
+        __syncthreads();  // the stage and the weight tile are reused by the next unit
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kScalarBlock) void prefill_scalar(PrefillParams p, int tiles_per_seq, int64_t units) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int i = (int)(unit / tiles_per_seq);
+        const int c = (int)(unit - (int64_t)i * tiles_per_seq) * kScalarBlock + (int)threadIdx.x;
+        int a = 0, e = p.t;
+        bool ok = true;
+        if (p.starts != nullptr) {
+            a = p.starts[i];
+            e = p.starts[i + 1];
+            ok = a >= 0 && a <= e && e <= p.t && (i > 0 || a == 0) && (i < p.n - 1 || e == p.t);
+            if (!ok && p.status != nullptr && threadIdx.x == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
+        }
+        const int slot = ok ? route_row(p.idx, p.status, p.n, p.s, i, lane) : -2;
+        if (c >= p.d || !ok) continue;
+        const int len = e - a;
+        const uint16_t *xc = (p.starts != nullptr ? p.x + (int64_t)a * p.xs_t : p.x + (int64_t)i * p.xs_n) +
+                             (int64_t)c * p.xs_d;
+        uint16_t *oc = (p.starts != nullptr ? p.out + (int64_t)a * p.os_t : p.out + (int64_t)i * p.os_n) +
+                       (int64_t)c * p.os_d;
+        if (slot < 0) {  // padding (or rejected) sequence
+            for (int j = 0; j < len; ++j) oc[(int64_t)j * p.os_t] = 0;
+            continue;
+        }
+        const bool stateful = p.state != nullptr;
+        const bool from_state = stateful && p.has_init != nullptr && p.has_init[i] != 0;
+        const int L = stateful ? p.l : 3;
+        uint16_t *h = stateful ? p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d : nullptr;
+        const int64_t sl = p.st_l;
+        const uint16_t *wt = p.weight + (int64_t)c * 4;
+        const float w0 = bf16_bits_to_f32(wt[0]), w1 = bf16_bits_to_f32(wt[1]);
+        const float w2 = bf16_bits_to_f32(wt[2]), w3 = bf16_bits_to_f32(wt[3]);
+        const float b = p.bias != nullptr ? bf16_bits_to_f32(p.bias[c]) : 0.0f;
+        float h0 = from_state ? bf16_bits_to_f32(h[(L - 3) * sl]) : 0.0f;
+        float h1 = from_state ? bf16_bits_to_f32(h[(L - 2) * sl]) : 0.0f;
+        float h2 = from_state ? bf16_bits_to_f32(h[(L - 1) * sl]) : 0.0f;
+        for (int j = 0; j < len; ++j) {
+            const float xv = bf16_bits_to_f32(xc[(int64_t)j * p.xs_t]);
+            float acc = h0 * w0;
+            acc = __builtin_fmaf(h1, w1, acc);
+            acc = __builtin_fmaf(h2, w2, acc);
+            acc = __builtin_fmaf(xv, w3, acc);
+            acc += b;
+            oc[(int64_t)j * p.os_t] = f32_to_bf16_bits(activate<ACT>(acc));
+            h0 = h1;
+            h1 = h2;
+            h2 = xv;
+        }
+        if (stateful) {
+            // final position k is ext[len + k]: a token, or (len + k < L) the initial
+            // value at position len + k, read before it is overwritten (len + k >= k)
+            for (int k = 0; k < L; ++k) {
+                const int m = len + k;
+                uint16_t v = 0;
+                if (m >= L)
+                    v = xc[(int64_t)(m - L) * p.xs_t];
+                else if (from_state)
+                    v = h[(int64_t)m * sl];
+                h[(int64_t)k * sl] = v;
+            }
+        }
+    }
+}
+
+template <typename Kernel, typename... Args>
+hipError_t launch(Kernel kernel, int64_t blocks, int block, hipStream_t stream, Args... args) {
+    void *argv[] = {&args...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(block), argv, 0,
+                           stream);
+}
+
+template <int ACT>
+hipError_t launch_chunks(const PrefillParams &p, int tiles, hipStream_t stream) {
+    const int64_t units_per_seq = ((int64_t)p.t + kChunk - 1) / kChunk;
+    const int64_t units = p.starts != nullptr ? units_per_seq : units_per_seq * p.n;
+    if (units == 0) return hipSuccess;
+    const int64_t n_blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+    const int64_t v_blocks = (n_blocks + kXcds - 1) / kXcds * kXcds;
+    const int64_t grid = v_blocks < kMaxBlocks ? v_blocks : kMaxBlocks;  // kMaxBlocks is a multiple of 8
+    PrefillParams pp = p;
+    return p.bias != nullptr
+               ? launch(prefill_chunks_v8<ACT, true>, grid, kBlock, stream, pp, tiles, units, units_per_seq, n_blocks,
+                        v_blocks)
+               : launch(prefill_chunks_v8<ACT, false>, grid, kBlock, stream, pp, tiles, units, units_per_seq,
+                        n_blocks, v_blocks);
+}
+
+template <int L, int ACT, int LAYOUT>
+hipError_t launch_edges(const PrefillParams &p, int tiles, hipStream_t stream) {
+    const int64_t block_units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+    const int64_t grid = block_units < kMaxBlocks ? block_units : kMaxBlocks;
+    PrefillParams pp = p;
+    return launch(prefill_edges_v8<L, ACT, LAYOUT>, grid, kBlock, stream, pp, tiles, block_units);
+}
+
+template <int ACT, int LAYOUT>
+hipError_t launch_edges_l(const PrefillParams &p, int tiles, hipStream_t stream, const char **name) {
+#define DCCONV_PF_NAME(LL)                                                                                        \
+    (LAYOUT == kStateless                                                                                         \
+         ? (ACT ? "prefill_edges_v8<stateless,silu>+prefill_chunks_v8<silu>"                                      \
+                : "prefill_edges_v8<stateless,identity>+prefill_chunks_v8<identity>")                             \
+         : LAYOUT == kCompactState                                                                                \
+               ? (ACT ? "prefill_edges_v8<L=" #LL ",silu,compact>+prefill_chunks_v8<silu>"                        \
+                      : "prefill_edges_v8<L=" #LL ",identity,compact>+prefill_chunks_v8<identity>")               \
+               : (ACT ? "prefill_edges_v8<L=" #LL ",silu,channel_last>+prefill_chunks_v8<silu>"                   \
+                      : "prefill_edges_v8<L=" #LL ",identity,channel_last>+prefill_chunks_v8<identity>"))
+#define DCCONV_PF_CASE(LL)                                 \
+    case LL:                                               \
+        *name = DCCONV_PF_NAME(LL);                        \
+        return launch_edges<LL, ACT, LAYOUT>(p, tiles, stream);
+    if (LAYOUT == kStateless) {
+        *name = DCCONV_PF_NAME(3);
+        return launch_edges<3, ACT, kStateless>(p, tiles, stream);
+    }
+    switch (p.l) {
+        DCCONV_PF_CASE(3)
+        DCCONV_PF_CASE(4)
+        DCCONV_PF_CASE(5)
+        DCCONV_PF_CASE(6)
+        DCCONV_PF_CASE(7)
+        DCCONV_PF_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef DCCONV_PF_CASE
+#undef DCCONV_PF_NAME
+}
+
+template <int ACT>
+hipError_t launch_prefill_v8(const PrefillParams &p, StateLayout layout, hipStream_t stream, const char **name) {
+    const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
+    hipError_t err;
+    if (p.state == nullptr)
+        err = launch_edges_l<ACT, kStateless>(p, tiles, stream, name);
+    else if (layout == StateLayout::ChannelLast)
+        err = launch_edges_l<ACT, kChannelLastState>(p, tiles, stream, name);
+    else
+        err = launch_edges_l<ACT, kCompactState>(p, tiles, stream, name);
+    if (err != hipSuccess) return err;
+    return launch_chunks<ACT>(p, tiles, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams &p, StateLayout layout, int activation, hipStream_t stream,
+                          const char **kernel_name) {
+    const bool silu = activation == DCCONV_ACT_SILU;
+    const int64_t lim = (int64_t)1 << 30;
+    const bool stateful = p.state != nullptr;
+    // The vector path needs 16-byte channel vectors everywhere and every buffer
+    // descriptor below 2^30 bytes (see kBadToken / kBadLane): a chunk with its
+    // halo, the 3 head or L tail tokens of the edges, the L state planes.
+    const bool v8 = p.d % kChPerLane == 0 && p.xs_d == 1 && p.os_d == 1 && p.xs_t % 8 == 0 && p.os_t % 8 == 0 &&
+                    (p.starts != nullptr || p.n == 1 || (p.xs_n % 8 == 0 && p.os_n % 8 == 0)) &&
+                    p.xs_t * 2 * (int64_t)(kChunk + 3) + 2 * kChPerWave < lim &&
+                    p.os_t * 2 * (int64_t)(kChunk + 3) + 2 * kChPerWave < lim &&
+                    (!stateful || (p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8 &&
+                                   p.st_l * 2 * (int64_t)p.l + 2 * kChPerWave < lim));
+    if (v8) return silu ? launch_prefill_v8<DCCONV_ACT_SILU>(p, layout, stream, kernel_name)
+                        : launch_prefill_v8<DCCONV_ACT_IDENTITY>(p, layout, stream, kernel_name);
+    const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
+    const int64_t units = (int64_t)p.n * tiles;
+    const int64_t grid = units < kMaxBlocks ? units : kMaxBlocks;
+    *kernel_name = silu ? "prefill_scalar<silu>" : "prefill_scalar<identity>";
+    PrefillParams pp = p;
+    return silu ? launch(prefill_scalar<DCCONV_ACT_SILU>, grid, kScalarBlock, stream, pp, tiles, units)
+                : launch(prefill_scalar<DCCONV_ACT_IDENTITY>, grid, kScalarBlock, stream, pp, tiles, units);
+}
+
+}  // namespace dcconv

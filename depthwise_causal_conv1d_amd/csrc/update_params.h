@@ -1,5 +1,5 @@
-// Internal interface between the C-ABI front end (abi.hip) and the update
-// kernels (update.hip).  Not part of the public ABI.
+// Internal interface between the C-ABI front end (abi.hip) and the kernels
+// (update.hip, update_tokens.hip, prefill.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +39,24 @@ struct TokensParams {
     int32_t n, d, t, s, l;
 };
 
+// A prefill: n sequences (batch form, or packed with `starts`), validated on the
+// host.  state == nullptr means stateless (no initial and no final state).
+struct PrefillParams {
+    const uint16_t *x;
+    uint16_t *state;
+    const uint16_t *weight;
+    const uint16_t *bias;
+    const int32_t *starts;   // int32 [n+1] or nullptr (batch form)
+    const int32_t *idx;
+    const uint8_t *has_init;
+    int32_t *status;
+    uint16_t *out;
+    int64_t xs_n, xs_d, xs_t;
+    int64_t os_n, os_d, os_t;
+    int64_t st_s, st_d, st_l;
+    int32_t n, d, t, s, l;
+};
+
 // Picks the specialisation, launches it on `stream` and stores its name in
 // *kernel_name.  Returns hipSuccess or the launch error.
 hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation,
@@ -46,5 +64,8 @@ hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activati
 
 hipError_t launch_update_tokens(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
                                 const char **kernel_name);
+
+hipError_t launch_prefill(const PrefillParams &p, StateLayout layout, int activation, hipStream_t stream,
+                          const char **kernel_name);
 
 }  // namespace dcconv

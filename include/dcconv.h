@@ -56,7 +56,9 @@ enum { DCCONV_ACT_IDENTITY = 0, DCCONV_ACT_SILU = 1 };
 /* Bits OR-ed into *dev_status by the device when a routing entry is rejected. */
 enum {
     DCCONV_DEV_BAD_INDEX = 1, /* an index below -1, or not below S           */
-    DCCONV_DEV_DUP_INDEX = 2  /* two rows of the batch select one real slot  */
+    DCCONV_DEV_DUP_INDEX = 2, /* two rows of the batch select one real slot  */
+    DCCONV_DEV_BAD_SEQ = 4    /* dcconv_prefill: seq_starts is not 0 = starts[0]
+                                 <= starts[1] <= ... <= starts[n] = t          */
 };
 
 /* The DCCONV_ABI_VERSION the library was built with. */
@@ -166,6 +168,68 @@ int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t t,
                          void *out, int64_t os_n, int64_t os_d, int64_t os_t,
                          int32_t *dev_status,
                          void *stream);
+
+/*
+ * dcconv_prefill -- full-sequence causal convolution (prefill), returning the
+ * final state that dcconv_update continues.
+ *
+ * The decode page names this operation at its top (cudnn.ops.causal_conv1d, for
+ * full sequences; its width-four final state is handed to the update, section
+ * "Semantic tensor contract": an L=3 state from prefill is accepted in place).
+ * Its own page is not among the sources; this follows the plainest reading the
+ * decode page supports.  For sequence i (slot s) and channel c:
+ *
+ *     ext          = concat(init[0:L], x[i, c, 0:T_i])     init = slot s's state or zeros
+ *     out[i, c, j] = act(sum_k ext[L + j - 3 + k] * weight[c, k] + bias[c])
+ *     slot s       = ext[T_i : T_i + L]                     (the newest L values)
+ *
+ * Sequences -- two forms:
+ *   seq_starts == NULL  n sequences of t tokens each; token j of sequence i,
+ *                       channel c at x[i*xs_n + c*xs_d + j*xs_t] (out likewise).
+ *   seq_starts != NULL  device int32 [n+1], 0 = starts[0] <= ... <= starts[n] = t:
+ *                       sequence i is packed tokens starts[i] .. starts[i+1]-1,
+ *                       token p at x[c*xs_d + p*xs_t]; xs_n and os_n are unused.
+ *                       A table that breaks the ordering sets DCCONV_DEV_BAD_SEQ
+ *                       in *dev_status; outputs and states are then unspecified
+ *                       (every access still stays inside the operands).
+ * State:
+ *   conv_state == NULL  no initial and no final state (history starts at zero);
+ *                       s must be 0, conv_state_indices and has_initial_state
+ *                       NULL; l and st_* are ignored.
+ *   conv_state != NULL  [s, d, l] at strides (st_s, st_d, st_l), compact or
+ *                       channel-last as for dcconv_update (channel-last l = 3 is
+ *                       the hand-off layout).  Sequence i uses slot
+ *                       conv_state_indices[i] (or i); -1 is a padding sequence:
+ *                       zero outputs, no slot touched; bad and duplicate indices
+ *                       as for dcconv_update.  The final state replaces the slot.
+ *   has_initial_state   device uint8 [n] or NULL.  Nonzero: sequence i continues
+ *                       from its slot's state; zero or NULL: from zeros.
+ * x, out           BF16 at element strides >= 0; out must give every element its
+ *                  own address.  16-byte aligned; seq_starts 4-byte aligned.
+ *                  Nothing the call writes may overlap any other operand.
+ * weight, w, bias, activation, dev_status, stream: as for dcconv_update.
+ *
+ * t == 0 (or every sequence empty) still writes the final states (the initial
+ * state unchanged, or zeros).  n == 0: DCCONV_OK, nothing enqueued.
+ * The fast path needs d % 8 == 0, unit channel strides, token and row strides
+ * that are multiples of 8 and 3 <= l <= 8; other shapes take a per-element path.
+ *
+ * Returns DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED or DCCONV_EHIP, with the
+ * same meanings as for dcconv_update.
+ */
+int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
+                   int64_t xs_n, int64_t xs_d, int64_t xs_t,
+                   const int32_t *seq_starts,
+                   void *conv_state, int64_t s, int64_t l,
+                   int64_t st_s, int64_t st_d, int64_t st_l,
+                   const int32_t *conv_state_indices,
+                   const uint8_t *has_initial_state,
+                   const void *weight, int64_t w,
+                   const void *bias,
+                   int activation,
+                   void *out, int64_t os_n, int64_t os_d, int64_t os_t,
+                   int32_t *dev_status,
+                   void *stream);
 
 #ifdef __cplusplus
 }

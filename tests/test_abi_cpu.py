@@ -253,3 +253,63 @@ def test_tokens_frontend_needs_3d_x():
     _, st, w = _cpu_args()
     with pytest.raises(ValueError, match=r"\[N, D, T\]"):
         dc.causal_conv1d_update_tokens(torch.zeros(4, 16, dtype=torch.bfloat16), st, w)
+
+
+# ----------------------------------------------------------- prefill entry point
+
+SEQ, HI = 0x90000000, 0xA0000000
+
+
+def _pargs(**over):
+    a = dict(x=X, n=4, d=64, t=10, xs_n=640, xs_d=1, xs_t=64, seq_starts=None, conv_state=ST, s=4, l=3, st_s=192,
+             st_d=1, st_l=64, conv_state_indices=None, has_initial_state=None, weight=WT, w=4, bias=None,
+             activation=1, out=OUT, os_n=640, os_d=1, os_t=64, dev_status=None, stream=None)
+    a.update(over)
+    return a
+
+
+PREFILL_DECLINES = [
+    (dict(t=-1), dc.DCCONV_EINVAL, "t (tokens)"),
+    (dict(xs_t=-64), dc.DCCONV_EINVAL, "non-negative"),
+    (dict(conv_state=None), dc.DCCONV_EINVAL, "without conv_state"),                 # s = 4 without a state
+    (dict(conv_state=None, s=0, conv_state_indices=IX), dc.DCCONV_EINVAL, "without conv_state"),
+    (dict(conv_state=None, s=0, has_initial_state=HI), dc.DCCONV_EINVAL, "without conv_state"),
+    (dict(w=3), dc.DCCONV_EUNSUPPORTED, "w=4"),
+    (dict(l=2, st_l=64, st_s=128), dc.DCCONV_EINVAL, "must be >= w-1"),
+    (dict(os_t=32), dc.DCCONV_EINVAL, "same address"),
+    (dict(seq_starts=SEQ + 2, n=3, xs_n=0), dc.DCCONV_EINVAL, "4-byte aligned"),
+    (dict(out=SEQ - 64, seq_starts=SEQ, n=3), dc.DCCONV_EINVAL, "overlaps seq_starts"),
+    (dict(conv_state=HI - 256, has_initial_state=HI), dc.DCCONV_EINVAL, "overlaps has_initial_state"),
+    (dict(out=X + 1024), dc.DCCONV_EINVAL, "overlaps"),
+    (dict(x=X + 8), dc.DCCONV_EINVAL, "16-byte aligned"),
+    (dict(s=3), dc.DCCONV_EINVAL, "must be >= n"),
+    (dict(st_d=2, st_l=1, st_s=192), dc.DCCONV_EUNSUPPORTED, "neither compact"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code,frag", PREFILL_DECLINES, ids=[str(d[0]) for d in PREFILL_DECLINES])
+def test_prefill_host_refusals(over, code, frag):
+    rc = dc.dcconv_prefill(**_pargs(**over))
+    assert rc == code, (rc, dc.dcconv_last_error())
+    assert frag in dc.dcconv_last_error()
+
+
+@no_gpu
+def test_prefill_nothing_to_do_enqueues_nothing():
+    assert dc.dcconv_prefill(**_pargs(n=0, x=None, out=None)) == dc.DCCONV_OK
+    assert dc.dcconv_last_kernel() == ""
+    # stateless and no tokens: nothing to read or write
+    assert dc.dcconv_prefill(**_pargs(t=0, x=None, out=None, conv_state=None, s=0)) == dc.DCCONV_OK
+    assert dc.dcconv_last_kernel() == ""
+
+
+def test_prefill_frontend_checks():
+    x = torch.zeros(2, 16, 5, dtype=torch.bfloat16)
+    w = torch.zeros(16, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"\[N, D, T\]"):
+        dc.causal_conv1d(x[:, :, 0], w)
+    with pytest.raises(ValueError, match="on a GPU"):
+        dc.causal_conv1d(x, w)
+    with pytest.raises(NotImplementedError, match="inference only"):
+        dc.causal_conv1d(x.clone().float().requires_grad_(), w)
