@@ -46,7 +46,8 @@ def log(*a):
 def kernel_source_hash(kernel: str) -> str:
     """Hash of the sources a kernel is compiled from (its file and the shared
     device helpers), so stale counter summaries are recognised."""
-    main = "update_tokens.hip" if kernel.startswith("tokens_") else "update.hip"
+    main = ("update_tokens.hip" if kernel.startswith("tokens_") else
+            "prefill.hip" if kernel.startswith("prefill_") else "update.hip")
     h = hashlib.sha256()
     for name in (main, "device_common.h"):
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -57,7 +58,7 @@ def kernel_source_hash(kernel: str) -> str:
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none or the kernel source changed since the counters were taken."""
-    safe = kernel.split("<")[0]
+    safe = kernel.split("<")[0].replace("_edges", "")  # a prefill call is edges + chunks: "prefill_v8"
     path = os.path.join(PROFILES, f"traffic_{safe}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -129,12 +130,69 @@ class Workload:
                                     self.spec.act, out=s["out"][:, 0, :], conv_state_indices=s["idx"])
 
 
+class PrefillWorkload:
+    """Device buffer sets for one prefill workload (x, out and the state pool),
+    cycled per step; the state's initial values change from step to step (each
+    call's final state is the next one's initial state), which the cost does not
+    depend on."""
+
+    def __init__(self, spec, rotate_bytes: float, dev):
+        import numpy as np
+        import torch
+        from depthwise_causal_conv1d_amd import workloads as wl
+
+        self.spec = spec
+        data = wl.make_prefill(spec)
+        self.host = data
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        total, D = data["total"], spec.D
+        set_bytes = 4 * total * D + (data["state"].nbytes if data["state"] is not None else 0)
+        self.n_sets = min(128, max(1, int(math.ceil(rotate_bytes / set_bytes))))
+        self.set_bytes = set_bytes
+        self.tokens = 1
+        self.rows = total
+        packed = spec.lens is not None
+        self.weight = up(data["weight"])
+        self.bias = None if data["bias"] is None else up(data["bias"])
+        self.idx = None if data["indices"] is None else torch.from_numpy(data["indices"]).to(dev)
+        self.has_init = None if data["has_init"] is None else torch.from_numpy(data["has_init"]).to(dev)
+        self.starts = None if data["starts"] is None else torch.from_numpy(data["starts"]).to(dev)
+        self.sets = []
+        for _ in range(self.n_sets):
+            xb = up(data["x"])
+            x = xb.view(1, total, D).permute(0, 2, 1) if packed else xb.permute(0, 2, 1)
+            ob = torch.empty_like(xb)
+            out = ob.view(1, total, D).permute(0, 2, 1) if packed else ob.permute(0, 2, 1)
+            st = None
+            if data["state"] is not None:
+                st = up(data["state"])
+                if spec.layout == "channel_last":
+                    st = st.permute(0, 2, 1)
+            self.sets.append(dict(x=x, out=out, state=st))
+        self.bytes_per_call = wl.prefill_algorithmic_bytes(spec, data["has_init"])
+
+    def step(self, i: int):
+        import depthwise_causal_conv1d_amd as dc
+
+        s = self.sets[i % self.n_sets]
+        dc.causal_conv1d(s["x"], self.weight, self.bias, self.spec.act, conv_state=s["state"],
+                         conv_state_indices=self.idx, has_initial_state=self.has_init, seq_starts=self.starts,
+                         out=s["out"])
+
+
 def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
     import torch
     import depthwise_causal_conv1d_amd as dc
+    from depthwise_causal_conv1d_amd import workloads as wl
 
     dev = torch.device("cuda", torch.cuda.current_device())
-    wk = Workload(spec, rotate_mb * 2 ** 20, dev)
+    if isinstance(spec, wl.PrefillSpec):
+        wk = PrefillWorkload(spec, rotate_mb * 2 ** 20, dev)
+    else:
+        wk = Workload(spec, rotate_mb * 2 ** 20, dev)
     for i in range(warmup):
         wk.step(i)
     kernel = dc.dcconv_last_kernel()
@@ -167,7 +225,8 @@ def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
     ms = start.elapsed_time(end) / steps
     res = dict(workload=spec.name, kernel=kernel, ms_per_step=ms, us_per_call=ms * 1e3,
                wall_ms_per_step=wall * 1e3 / steps, bytes_per_call=wk.bytes_per_call,
-               gbs=wk.bytes_per_call / (ms * 1e-3) / 1e9, rows_per_s=spec.N * wk.tokens / (ms * 1e-3),
+               gbs=wk.bytes_per_call / (ms * 1e-3) / 1e9,
+               rows_per_s=getattr(wk, "rows", spec.N * wk.tokens) / (ms * 1e-3),
                tokens_per_call=wk.tokens,
                buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
     res["frac"] = res["gbs"] / PEAK_HBM_GBS
@@ -183,6 +242,8 @@ def cpu_baseline(spec, host, seconds: float):
     import oracle
     from depthwise_causal_conv1d_amd import workloads as wl
 
+    if isinstance(spec, wl.PrefillSpec):
+        return cpu_baseline_prefill(spec, host, seconds)
     tokens = spec.T if spec.one_call else 1
     x = np.ascontiguousarray(host["x"][0]) if tokens == 1 else np.ascontiguousarray(host["x"])
     reps, t_total = 0, 0.0
@@ -205,6 +266,56 @@ def cpu_baseline(spec, host, seconds: float):
             "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}, {tokens} token(s)) "
                       f"on host arrays, single thread, {per_call * 1e3:.1f} ms per call",
             "rows_per_s": spec.N * tokens / per_call}
+
+
+def cpu_baseline_prefill(spec, host, seconds: float):
+    """The oracle's prefill (single thread) on the first sequences of the workload,
+    as many as take about ``seconds``; reported per token."""
+    import numpy as np
+    import oracle
+    from depthwise_causal_conv1d_amd import workloads as wl
+
+    lens = list(spec.lens) if spec.lens is not None else [spec.T] * spec.N
+    D = spec.D
+    strides = wl.state_strides(spec) if spec.layout != "none" else (0, 0, 0)
+    x = host["x"].reshape(-1, D)
+    reps, t_total, toks, bytes_done, p0 = 0, 0.0, 0, 0, 0
+    for i, t in enumerate(lens):
+        xi = np.ascontiguousarray(x[p0:p0 + t])
+        p0 += t
+        st = None if host["state"] is None else host["state"].copy()
+        idx = None if host["indices"] is None else host["indices"][i:i + 1].copy()
+        hi = None if host["has_init"] is None else host["has_init"][i:i + 1].copy()
+        t0 = time.perf_counter()
+        oracle.prefill(xi, 1, D, t, (t * D, 1, D), host["weight"], host["bias"], spec.act, state_buf=st,
+                       S=spec.S if st is not None else 0, L=spec.L if st is not None else 0, state_strides=strides,
+                       indices=idx if idx is not None else (np.array([i], np.int32) if st is not None else None),
+                       has_init=hi)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        toks += t
+        bytes_done += 4 * t * D + 2 * D * spec.L
+        if t_total >= seconds:
+            break
+    return {"value": bytes_done / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {reps} sequences ({toks} tokens, D={D}) of {spec.name} on host arrays, "
+                      f"single thread, {t_total * 1e3 / max(toks, 1):.3f} ms per token",
+            "rows_per_s": toks / t_total}
+
+
+def config_of(spec, res, launch):
+    """The workload as a config object (no model keys)."""
+    import dataclasses
+    cfg = {"workload": spec.name}
+    for k, v in dataclasses.asdict(spec).items():
+        if k in ("name", "seed"):
+            continue
+        cfg[k] = list(v) if isinstance(v, tuple) else v
+    cfg["activation"] = cfg.pop("act", None) or "identity"
+    cfg["accumulate"] = "f32"
+    cfg["buffer_sets"] = res["buffer_sets"]
+    cfg["launch"] = "hipgraph" if launch == "graph" else "eager"
+    return cfg
 
 
 def environment():
@@ -280,10 +391,13 @@ def main():
         f"{res['buffer_sets']} buffer sets, wall {res['wall_ms_per_step'] * 1e3:.3f} us/step")
     others = []
     if not args.no_other_workloads:
-        for other in wl.CONFIGS + wl.EXTRA:
+        for other in wl.CONFIGS + wl.EXTRA + wl.PREFILL:
             if other.name == spec.name:
                 continue
-            r, _ = measure(other, max(200, args.steps // 5), 20, min(args.rotate_mb, 512.0), args.launch)
+            if isinstance(other, wl.PrefillSpec):  # ~60 us calls: fewer steps, sets beyond the 256 MB cache
+                r, _ = measure(other, max(20, args.steps // 20), 5, max(args.rotate_mb, 1024.0), args.launch)
+            else:
+                r, _ = measure(other, max(200, args.steps // 5), 20, min(args.rotate_mb, 512.0), args.launch)
             log(f"[bench] {other.name}: {r['us_per_call']:.3f} us/call, {r['gbs']:.1f} GB/s, "
                 f"{r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}")
             entry = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
@@ -310,10 +424,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "N": spec.N, "D": spec.D, "W": spec.W, "L": spec.L, "S": spec.S,
-                   "ld": spec.ld, "activation": spec.act or "identity", "bias": spec.bias,
-                   "indices": spec.routing != "none", "accumulate": "f32",
-                   "buffer_sets": res["buffer_sets"], "launch": "hipgraph" if args.launch == "graph" else "eager"},
+        "config": config_of(spec, res, args.launch),
         "rows_per_s": res["rows_per_s"],
         "us_per_call": res["us_per_call"],
         "bytes_per_call": res["bytes_per_call"],

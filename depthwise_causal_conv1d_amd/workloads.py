@@ -155,3 +155,94 @@ def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bo
     read_positions = L if layout == "compact" else L - min(T, L - (W - 1))
     return (2 * A * D * T + 2 * A * D * read_positions + 2 * A * D * L + 2 * D * W
             + (2 * D if bias else 0) + 2 * N * D * T + (4 * N if indices else 0))
+
+
+# ------------------------------------------------------------------- prefill
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillSpec:
+    """A full-sequence prefill workload: n sequences of T tokens (batch form), or
+    packed sequences of the given lengths."""
+    name: str
+    N: int                        # sequences
+    D: int
+    W: int
+    L: int
+    T: int = 0                    # tokens per sequence (batch form)
+    lens: Optional[tuple] = None  # packed form: tokens of each sequence
+    S: int = 0                    # state slots (0: no state)
+    layout: str = "channel_last"  # "channel_last", "compact" or "none" (stateless)
+    act: Optional[str] = "silu"
+    bias: bool = False
+    routing: str = "none"         # "none" (sequence i -> slot i) or "unique"
+    has_init: str = "none"        # "none", "all" or "mixed" (about 60 % continue from their slot)
+    seed: int = 0
+
+
+def _packed_lengths(rng, n, lo, hi):
+    return tuple(int(v) for v in rng.integers(lo, hi + 1, size=n))
+
+
+# A prefill batch of the width-four short convolution at the large decode
+# batch's width, handing its L=3 final state off channel-last; and packed
+# sequences of mixed lengths continuing from slots of a compact L=4 pool.
+PREFILL = [
+    PrefillSpec("prefill_batch", N=8, D=8192, W=4, L=3, T=2048, S=8, layout="channel_last", act="silu",
+                seed=11),
+    PrefillSpec("prefill_varlen", N=16, D=4096, W=4, L=4, lens=_packed_lengths(np.random.default_rng(12), 16, 1, 2048),
+                S=64, layout="compact", act="silu", bias=True, routing="unique", has_init="mixed", seed=12),
+]
+BY_NAME.update({c.name: c for c in PREFILL})
+
+
+def make_prefill(spec: PrefillSpec, seed: Optional[int] = None) -> dict:
+    """Draw one prefill workload.  Order of draws: x, weight, state, bias, indices,
+    has_init.  x is token-major: [total_tokens, D] (packed) or [N, T, D]."""
+    rng = np.random.default_rng(spec.seed if seed is None else seed)
+    packed = spec.lens is not None
+    total = sum(spec.lens) if packed else spec.N * spec.T
+    x = f32_to_bf16_bits(_normal(rng, (total, spec.D)))
+    if not packed:
+        x = x.reshape(spec.N, spec.T, spec.D)
+    weight = f32_to_bf16_bits(rng.uniform(-0.5, 0.5, size=(spec.D, spec.W)).astype(np.float32))
+    state = None
+    if spec.layout == "channel_last":
+        state = f32_to_bf16_bits(_normal(rng, (spec.S, spec.L, spec.D)))
+    elif spec.layout == "compact":
+        state = f32_to_bf16_bits(_normal(rng, (spec.S, spec.D, spec.L)))
+    bias = f32_to_bf16_bits(_normal(rng, (spec.D,), 0.1)) if spec.bias else None
+    indices = rng.choice(spec.S, spec.N, replace=False).astype(np.int32) if spec.routing == "unique" else None
+    if spec.has_init == "all":
+        has_init = np.ones(spec.N, np.uint8)
+    elif spec.has_init == "mixed":
+        has_init = (rng.random(spec.N) < 0.6).astype(np.uint8)
+    else:
+        has_init = None
+    starts = np.concatenate([[0], np.cumsum(spec.lens)]).astype(np.int32) if packed else None
+    return {"x": x, "weight": weight, "state": state, "bias": bias, "indices": indices, "has_init": has_init,
+            "starts": starts, "total": total}
+
+
+def prefill_algorithmic_bytes(spec: PrefillSpec, has_init=None) -> int:
+    """Bytes one prefill call must move at minimum: every token read once and its
+    output written once, each sequence's final state written, the initial state
+    read where a sequence continues from its slot (compact: all L values, which
+    are adjacent; channel-last: the planes still needed, L - min(T_i, L - (W-1))),
+    weight, bias and the small tables.  The 3-token halo a parallel kernel re-reads
+    between chunks is not counted."""
+    lens = list(spec.lens) if spec.lens is not None else [spec.T] * spec.N
+    D, L, W = spec.D, spec.L, spec.W
+    b = 4 * sum(lens) * D + 2 * D * W + (2 * D if spec.bias else 0)
+    if spec.lens is not None:
+        b += 4 * (spec.N + 1)
+    if spec.routing != "none":
+        b += 4 * spec.N
+    if spec.layout != "none":
+        if has_init is not None:
+            b += spec.N
+        for i, t in enumerate(lens):
+            b += 2 * D * L
+            if has_init is not None and has_init[i]:
+                b += 2 * D * (L if spec.layout == "compact" else L - min(t, L - (W - 1)))
+    return b

@@ -74,3 +74,35 @@ def test_cpu_baseline_leg(name):
     res = bench.cpu_baseline(spec, wl.make(spec), seconds=0.0)
     assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "GB/s" and res["value"] > 0
     json.dumps(res)
+
+
+def test_prefill_bytes_by_hand():
+    # 8 sequences x 2048 tokens x 8192 channels: x read and out written once,
+    # the channel-last L=3 final states written, the weight read; no initial state
+    spec = wl.BY_NAME["prefill_batch"]
+    tok = 8 * 2048
+    assert wl.prefill_algorithmic_bytes(spec, None) == 4 * tok * 8192 + 8 * 2 * 8192 * 3 + 2 * 8192 * 4
+
+
+def test_prefill_bytes_count_initial_state_reads():
+    spec = wl.PrefillSpec("p", N=3, D=64, W=4, L=8, lens=(1, 4, 20), S=3, layout="channel_last", routing="unique")
+    none = wl.prefill_algorithmic_bytes(spec, np.zeros(3, np.uint8))
+    some = wl.prefill_algorithmic_bytes(spec, np.array([1, 1, 1], np.uint8))
+    # planes still needed: L - min(T_i, L - 3) = 7, 4, 3
+    assert some - none == 2 * 64 * (7 + 4 + 3)
+
+
+def test_prefill_workload_shapes():
+    for spec in wl.PREFILL:
+        d = wl.make_prefill(spec)
+        lens = spec.lens if spec.lens is not None else [spec.T] * spec.N
+        assert d["total"] == sum(lens)
+        assert d["x"].reshape(-1, spec.D).shape == (sum(lens), spec.D)
+        if d["starts"] is not None:
+            assert d["starts"][0] == 0 and d["starts"][-1] == d["total"] and np.all(np.diff(d["starts"]) >= 0)
+
+
+def test_cpu_baseline_prefill_leg():
+    spec = wl.BY_NAME["prefill_varlen"]
+    res = bench.cpu_baseline(spec, wl.make_prefill(spec), seconds=0.0)
+    assert res["kind"] == "oracle" and res["value"] > 0 and "sequences" in res["sample"]
