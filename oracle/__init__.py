@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
                                          vp, vp,                                 # indices, has_init
                                          vp, i64, vp, i32,                       # weight, w, bias, act
                                          vp, vp, i64, i64, i64]                  # out, out_f32, os_n, os_d, os_t
+            L.oracle_update_ring.restype = i32
+            L.oracle_update_ring.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64,
+                                             vp, i64, vp, vp, vp, i32, vp, vp]
             L.oracle_bf16_to_f32.restype = ctypes.c_float
             L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
             L.oracle_f32_to_bf16.restype = ctypes.c_uint16
@@ -209,6 +212,24 @@ def prefill(x_buf, n, d, t, x_strides, weight, bias=None, activation=None, *, st
                               _ptr(state_buf), S, L, state_strides[0], state_strides[1], state_strides[2],
                               _ptr(indices), _ptr(has_init), _ptr(weight), W, _ptr(bias), ACT[activation],
                               _ptr(out), _ptr(out_f32), os_[0], os_[1], os_[2])
+    if rc != OK:
+        raise OracleError(rc)
+    return (out, out_f32) if want_f32 else out
+
+
+def update_ring(x, n, d, ld, state_buf, S, L, strides, weight, bias, indices, cache_seqlens, activation,
+                want_f32=False):
+    """One decode step on circular-buffer state (``cache_seqlens`` int32 [N]:
+    tokens each row's slot has seen).  ``state_buf`` holds [S, D, L] at element
+    ``strides`` and is updated in place (one value per channel)."""
+    _need(state_buf, np.uint16, "state_buf"); _need(x, np.uint16, "x")
+    _need(cache_seqlens, np.int32, "cache_seqlens")
+    W = weight.shape[1]
+    out = np.zeros((n, d), dtype=np.uint16)
+    out_f32 = np.zeros((n, d), dtype=np.float32) if want_f32 else None
+    rc = lib().oracle_update_ring(_ptr(x), n, d, ld, _ptr(state_buf), S, L, strides[0], strides[1], strides[2],
+                                  _ptr(weight), W, _ptr(bias), _ptr(indices), _ptr(cache_seqlens), ACT[activation],
+                                  _ptr(out), _ptr(out_f32))
     if rc != OK:
         raise OracleError(rc)
     return (out, out_f32) if want_f32 else out

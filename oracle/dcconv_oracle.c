@@ -13,6 +13,8 @@
  * the reserved multi-token form).  The full-sequence prefill (oracle_prefill) is
  * the operation that page names at its top for whole sequences; its own page is
  * not among the sources, and the reading taken is stated above the function.
+ * The circular-buffer step (oracle_update_ring) serves the cache_seqlens keyword
+ * the same section reserves; the ring reading is stated above that function.
  *
  * Arithmetic: FP32, one rounding to BF16 at the end, as the accuracy contract of
  * this library fixes ("FP32-accumulated oracle rounded once").  The page itself
@@ -354,6 +356,83 @@ int oracle_prefill(const uint16_t *x, int64_t n_seqs, int64_t d, int64_t t,
     }
     free(slot_of_seq);
     free(ext);
+    return rc;
+}
+
+/*
+ * One decode step on circular-buffer state, selected by cache_seqlens.  The page
+ * reserves the keyword "for circular-buffer state" and fixes nothing else, so
+ * this takes the plainest ring reading: a slot whose row has seen c tokens keeps
+ * token i (i = c-L .. c-1) at state[s, d, i mod L]; the step's history is those
+ * L tokens followed by x (the same history as the shifting update), so
+ *
+ *   out[n, d]               = act(sum_j token[c+1-w+j] * weight[d, j] + bias[d])
+ *                             with token[c] = x[n, d] and the others read at
+ *                             positions (c+1-w+j) mod L, taken before any write;
+ *   state[s, d, c mod L]    = x[n, d]     (the oldest token is replaced; the
+ *                                          other L-1 values do not move)
+ *
+ * c = cache_seqlens[n] >= 0 (ORACLE_EARGS otherwise); routing and padding rows as
+ * for oracle_update.  Arguments as for oracle_update.
+ */
+int oracle_update_ring(const uint16_t *x, int64_t n_rows, int64_t d, int64_t ld,
+                       uint16_t *state, int64_t s_slots, int64_t l,
+                       int64_t st_s, int64_t st_d, int64_t st_l,
+                       const uint16_t *weight, int64_t w, const uint16_t *bias,
+                       const int32_t *indices, const int32_t *cache_seqlens, int activation,
+                       uint16_t *out, float *out_f32)
+{
+    if (n_rows < 0 || d < 1 || ld < d || s_slots < 0 || w < 1 || l < w - 1 || l < 1)
+        return ORACLE_EARGS;
+    if (activation != ORACLE_ACT_IDENTITY && activation != ORACLE_ACT_SILU)
+        return ORACLE_EARGS;
+    if (n_rows == 0)
+        return ORACLE_OK;
+    if (!x || !state || !weight || !out || !cache_seqlens)
+        return ORACLE_EARGS;
+    if (!indices && s_slots < n_rows)
+        return ORACLE_EARGS;
+    for (int64_t n = 0; n < n_rows; ++n)
+        if (cache_seqlens[n] < 0)
+            return ORACLE_EARGS;
+    int64_t *slot_of_row = (int64_t *)malloc((size_t)n_rows * sizeof(int64_t));
+    if (!slot_of_row)
+        return ORACLE_EARGS;
+    int rc = resolve_slots(indices, n_rows, s_slots, slot_of_row);
+    for (int64_t n = 0; rc == ORACLE_OK && n < n_rows; ++n) {
+        int64_t s = slot_of_row[n];
+        if (s == -1) {                       /* padding row: zero output, no mutation */
+            for (int64_t c = 0; c < d; ++c) {
+                out[n * d + c] = 0;
+                if (out_f32)
+                    out_f32[n * d + c] = 0.0f;
+            }
+            continue;
+        }
+        int64_t seen = cache_seqlens[n];
+        for (int64_t c = 0; c < d; ++c) {
+            uint16_t *ring = state + s * st_s + c * st_d;
+            uint16_t xb = x[n * ld + c];
+            float acc = 0.0f;
+            for (int64_t j = 0; j < w; ++j) {
+                int64_t tok = seen + 1 - w + j;              /* token index of tap j */
+                uint16_t v = xb;
+                if (tok < seen) {
+                    int64_t pos = ((tok % l) + l) % l;       /* non-negative remainder */
+                    v = ring[pos * st_l];
+                }
+                acc = acc + oracle_bf16_to_f32(v) * oracle_bf16_to_f32(weight[c * w + j]);
+            }
+            if (bias)
+                acc = acc + oracle_bf16_to_f32(bias[c]);
+            float y = act_apply(acc, activation);
+            if (out_f32)
+                out_f32[n * d + c] = y;
+            out[n * d + c] = oracle_f32_to_bf16(y);
+            ring[(seen % l) * st_l] = xb;
+        }
+    }
+    free(slot_of_row);
     return rc;
 }
 
