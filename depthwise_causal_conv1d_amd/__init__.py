@@ -29,12 +29,12 @@ __all__ = [
     "dcconv_abi_version", "dcconv_last_error", "dcconv_last_kernel", "dcconv_update",
     "dcconv_update_tokens", "causal_conv1d_update", "causal_conv1d_update_out",
     "causal_conv1d_update_tokens", "dcconv_prefill", "causal_conv1d", "library_path", "DcconvError",
-    "DCCONV_DEV_BAD_SEQ",
+    "DCCONV_DEV_BAD_SEQ", "DCCONV_DEV_BAD_SEQLEN",
 ]
 
 DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED, DCCONV_EHIP = 0, 1, 2, 3
 DCCONV_ACT_IDENTITY, DCCONV_ACT_SILU = 0, 1
-DCCONV_DEV_BAD_INDEX, DCCONV_DEV_DUP_INDEX, DCCONV_DEV_BAD_SEQ = 1, 2, 4
+DCCONV_DEV_BAD_INDEX, DCCONV_DEV_DUP_INDEX, DCCONV_DEV_BAD_SEQ, DCCONV_DEV_BAD_SEQLEN = 1, 2, 4, 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdcconv.so")
@@ -162,9 +162,6 @@ def _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlen
                    x_unit_channel_stride=True):
     import torch
 
-    if cache_seqlens is not None:
-        raise NotImplementedError("cache_seqlens is reserved and must be None "
-                                  "(circular-buffer state is not served)")
     for name, t in (("x", x), ("conv_state", conv_state), ("weight", weight), ("bias", bias),
                     ("conv_state_indices", conv_state_indices)):
         if t is not None and t.requires_grad:
@@ -196,9 +193,12 @@ def _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlen
     if conv_state_indices is not None and (conv_state_indices.dim() != 1 or conv_state_indices.shape[0] != N
                                            or not conv_state_indices.is_contiguous()):
         raise ValueError("conv_state_indices must be a contiguous int32 [N] tensor")
+    if cache_seqlens is not None and (cache_seqlens.dtype != torch.int32 or cache_seqlens.dim() != 1
+                                      or cache_seqlens.shape[0] != N or not cache_seqlens.is_contiguous()):
+        raise ValueError("cache_seqlens must be a contiguous int32 [N] tensor (tokens each row's slot has seen)")
     dev = x.device
     for name, t in (("conv_state", conv_state), ("weight", weight), ("bias", bias),
-                    ("conv_state_indices", conv_state_indices)):
+                    ("conv_state_indices", conv_state_indices), ("cache_seqlens", cache_seqlens)):
         if t is not None and t.device != dev:
             raise ValueError(f"{name} is on {t.device}, x on {dev}")
     if dev.type != "cuda":
@@ -224,7 +224,7 @@ def causal_conv1d_update_out(x, conv_state, weight, bias=None, activation=None, 
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
         rc = dcconv_update(_ptr(x), N, D, ld, _ptr(conv_state), S, L, st[0], st[1], st[2],
-                           _ptr(weight), weight.shape[1], _ptr(bias), _ptr(conv_state_indices), None,
+                           _ptr(weight), weight.shape[1], _ptr(bias), _ptr(conv_state_indices), _ptr(cache_seqlens),
                            _ACTIVATIONS[activation], _ptr(out), _ptr(dev_status), stream)
     _raise_for(rc)
     return out
@@ -233,13 +233,15 @@ def causal_conv1d_update_out(x, conv_state, weight, bias=None, activation=None, 
 def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None, *,
                          cache_seqlens=None, conv_state_indices=None):
     """One decode step: updates ``conv_state`` in place and returns a new bf16 [N, D]
-    output (page "Causal Conv1d Decode Update", section "Python API")."""
+    output (page "Causal Conv1d Decode Update", section "Python API").  With
+    ``cache_seqlens`` (int32 [N], tokens each row's slot has seen; not advanced
+    here) the state is a circular buffer: token i at position i mod L."""
     import torch
 
     _check_tensors(x, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation)
     out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     return causal_conv1d_update_out(x, conv_state, weight, bias, activation, out=out,
-                                    conv_state_indices=conv_state_indices)
+                                    cache_seqlens=cache_seqlens, conv_state_indices=conv_state_indices)
 
 
 def causal_conv1d_update_tokens(x, conv_state, weight, bias=None, activation=None, *, conv_state_indices=None,

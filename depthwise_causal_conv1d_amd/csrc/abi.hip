@@ -4,7 +4,8 @@
 //
 // Contract: cuDNN FE-OSS page "Causal Conv1d Decode Update", sections "Semantic
 // tensor contract" (shapes, the x row-stride rule, L >= W-1) and "Current native
-// implementation" (W = 4, alignment, cache_seqlens must be absent).  Contract
+// implementation" (W = 4, alignment); cache_seqlens selects the circular-buffer
+// state the page reserves that keyword for.  Contract
 // violations return DCCONV_EINVAL (the page's ValueError); valid requests that
 // are not served return DCCONV_EUNSUPPORTED (the page's NotImplementedError).
 #include <stdarg.h>
@@ -56,7 +57,7 @@ constexpr int64_t kI32Max = 2147483647;
 
 // Metadata shared by both entry points: shapes, state strides, the served subset.
 int check_state_and_shapes(int64_t n, int64_t d, int64_t s, int64_t l, int64_t st_s, int64_t st_d, int64_t st_l,
-                           int64_t w, int activation, const int32_t *cache_seqlens, dcconv::StateLayout *layout) {
+                           int64_t w, int activation, dcconv::StateLayout *layout) {
     if (n < 0) return fail(DCCONV_EINVAL, "n (decode rows) must be >= 0, got %lld", (long long)n);
     if (d < 1) return fail(DCCONV_EINVAL, "d (channels) must be >= 1, got %lld", (long long)d);
     if (s < 0) return fail(DCCONV_EINVAL, "s (state slots) must be >= 0, got %lld", (long long)s);
@@ -68,9 +69,6 @@ int check_state_and_shapes(int64_t n, int64_t d, int64_t s, int64_t l, int64_t s
         return fail(DCCONV_EINVAL, "activation must be DCCONV_ACT_IDENTITY (0) or DCCONV_ACT_SILU (1), got %d",
                     activation);
     if (st_s < 0 || st_d < 0 || st_l < 0) return fail(DCCONV_EINVAL, "conv_state strides must be non-negative");
-    if (cache_seqlens != nullptr)
-        return fail(DCCONV_EUNSUPPORTED,
-                    "cache_seqlens is reserved and must be NULL (circular-buffer state is not served)");
     if (w != 4) return fail(DCCONV_EUNSUPPORTED, "only filter width w=4 is served, got w=%lld", (long long)w);
     if (n > kI32Max || d > kI32Max || s > kI32Max || l > 65536)
         return fail(DCCONV_EUNSUPPORTED, "sizes beyond n, d, s < 2^31 and l <= 65536 are not served");
@@ -181,11 +179,14 @@ extern "C" int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
         return fail(DCCONV_EINVAL,
                     "padded x rows need ld_x %% 8 == 0 (16-byte aligned rows), got ld_x=%lld for d=%lld",
                     (long long)ld_x, (long long)d);
-    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, cache_seqlens, &layout);
+    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, &layout);
     if (rc != DCCONV_OK) return rc;
     if (n == 0) return succeed("");
+    if (cache_seqlens != nullptr && !aligned(cache_seqlens, 4))
+        return fail(DCCONV_EINVAL, "cache_seqlens must be 4-byte aligned");
+    const Span extra[] = {span("cache_seqlens", cache_seqlens, 4 * n)};
     rc = check_pointers(x, 2 * ((n - 1) * ld_x + d), conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias,
-                        conv_state_indices, n, out, 2 * n * d, dev_status);
+                        conv_state_indices, n, out, 2 * n * d, dev_status, extra, 1);
     if (rc != DCCONV_OK) return rc;
 
     dcconv::UpdateParams p;
@@ -194,6 +195,7 @@ extern "C" int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
     p.weight = static_cast<const uint16_t *>(weight);
     p.bias = static_cast<const uint16_t *>(bias);
     p.idx = conv_state_indices;
+    p.seqlens = cache_seqlens;
     p.status = dev_status;
     p.out = static_cast<uint16_t *>(out);
     p.ld = n > 1 ? ld_x : d;
@@ -227,8 +229,12 @@ extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t
     if (t < 0) return fail(DCCONV_EINVAL, "t (tokens) must be >= 0, got %lld", (long long)t);
     if (xs_n < 0 || xs_d < 0 || xs_t < 0 || os_n < 0 || os_d < 0 || os_t < 0)
         return fail(DCCONV_EINVAL, "x and out strides must be non-negative");
-    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, cache_seqlens, &layout);
+    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, &layout);
     if (rc != DCCONV_OK) return rc;
+    if (cache_seqlens != nullptr)
+        return fail(DCCONV_EUNSUPPORTED,
+                    "cache_seqlens (circular-buffer state) is served by dcconv_update only, not by the "
+                    "multi-token update");
     if (t > kI32Max) return fail(DCCONV_EUNSUPPORTED, "t >= 2^31 tokens is not served");
     if (n == 0 || t == 0) return succeed("");
     const int64_t ext[3] = {n, d, t}, ost[3] = {os_n, os_d, os_t};
@@ -299,7 +305,7 @@ extern "C" int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
         st_s = d * l;
     }
     dcconv::StateLayout layout;
-    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, nullptr, &layout);
+    int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, &layout);
     if (rc != DCCONV_OK) return rc;
     if (t > kI32Max) return fail(DCCONV_EUNSUPPORTED, "t >= 2^31 tokens is not served");
     if (n == 0) return succeed("");

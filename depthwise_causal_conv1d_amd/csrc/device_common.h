@@ -211,5 +211,24 @@ __device__ __forceinline__ void unpack_bias(const u32x4 &bv, float (&bf)[8]) {
     }
 }
 
+// out = act(w0*h0 + w1*h1 + w2*h2 + w3*xt + b) for the lane's 8 channels, in
+// the oracle's order (taps ascending, bias last); BF16 products are exact.
+template <int ACT>
+__device__ __forceinline__ u32x4 conv8(const u32x4 &h0, const u32x4 &h1, const u32x4 &h2, const u32x4 &xt,
+                                       const float (&wf)[32], const float (&bf)[8]) {
+    float y[kChPerLane];
+#pragma unroll
+    for (int ch = 0; ch < kChPerLane; ++ch) {
+        const int q = ch >> 1, hh = ch & 1;
+        float acc = half_f32(h0[q], hh) * wf[4 * ch + 0];
+        acc = __builtin_fmaf(half_f32(h1[q], hh), wf[4 * ch + 1], acc);
+        acc = __builtin_fmaf(half_f32(h2[q], hh), wf[4 * ch + 2], acc);
+        acc = __builtin_fmaf(half_f32(xt[q], hh), wf[4 * ch + 3], acc);
+        acc += bf[ch];
+        y[ch] = activate<ACT>(acc);
+    }
+    return u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+}
+
 }  // namespace
 }  // namespace dcconv

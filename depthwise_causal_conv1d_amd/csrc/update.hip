@@ -440,6 +440,7 @@ hipError_t launch_channel_last(const UpdateParams &p, int tiles, hipStream_t str
 
 hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation, hipStream_t stream,
                          const char **kernel_name) {
+    if (p.seqlens != nullptr) return launch_update_ring(p, layout, activation, stream, kernel_name);
     const bool rows_v8 = (p.d % kChPerLane == 0) && (p.ld % kChPerLane == 0);
     const bool silu = activation == DCCONV_ACT_SILU;
     const int tiles_v8 = (p.d + kChPerWave - 1) / kChPerWave;

@@ -14,6 +14,7 @@ struct UpdateParams {
     const uint16_t *weight; // BF16 [d, 4]
     const uint16_t *bias;   // BF16 [d] or nullptr
     const int32_t *idx;     // int32 [n] or nullptr
+    const int32_t *seqlens; // int32 [n] (circular-buffer state) or nullptr
     int32_t *status;        // device int32 or nullptr
     uint16_t *out;          // BF16 [n, d]
     int64_t ld;
@@ -61,6 +62,10 @@ struct PrefillParams {
 // *kernel_name.  Returns hipSuccess or the launch error.
 hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation,
                          hipStream_t stream, const char **kernel_name);
+
+// The circular-buffer form of launch_update (p.seqlens != nullptr).
+hipError_t launch_update_ring(const UpdateParams &p, StateLayout layout, int activation, hipStream_t stream,
+                              const char **kernel_name);
 
 hipError_t launch_update_tokens(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
                                 const char **kernel_name);

@@ -1,0 +1,165 @@
+// Decode step on circular-buffer state (cache_seqlens) for gfx950.
+//
+// The cuDNN FE-OSS page "Causal Conv1d Decode Update" reserves cache_seqlens for
+// circular-buffer state (section "Causal Conv1d Decode Update").  Ring reading:
+// a slot whose row has seen c = cache_seqlens[n] tokens keeps token i at
+// position i mod L.  The step's taps are tokens c-3, c-2, c-1 (positions
+// (c-3+k) mod L) and x; x then replaces the oldest token, at position c mod L.
+// Only one value per channel is written, instead of the L a shifting update
+// rewrites.
+//
+//  * update_ring_v8<ACT, HAS_BIAS>: channel-last state, where each position is a
+//    contiguous plane, so a row reads 3 planes and writes 1.  One wavefront per
+//    (row, 512-channel tile), 8 channels per lane; the block's two rows share
+//    the tile's weights.
+//  * update_ring_scalar<ACT>: one thread per (row, channel), any layout.
+#include <stdint.h>
+
+#include "dcconv.h"
+#include "device_common.h"
+#include "update_params.h"
+
+namespace dcconv {
+namespace {
+
+constexpr uint32_t kBadLane = 1u << 31;  // beyond every descriptor here (all < 2^30 bytes)
+
+// ((t mod L) + L) mod L for any t: the ring position of token t.
+__device__ __forceinline__ int ring_pos(int t, int L) {
+    const int r = t % L;
+    return r < 0 ? r + L : r;
+}
+
+// The row's slot, or -1 when it must not touch the state; a negative
+// cache_seqlens entry rejects the row and sets DCCONV_DEV_BAD_SEQLEN.  All 64
+// lanes of the wave call it; the result is wave-uniform.
+__device__ __forceinline__ int route_ring_row(const UpdateParams &p, int row, int lane, int *seen) {
+    const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
+    *seen = p.seqlens[row];
+    if (*seen < 0) {
+        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQLEN);
+        return -1;
+    }
+    return slot;
+}
+
+template <int ACT, bool HAS_BIAS>
+__global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int tiles, int64_t block_units) {
+    __shared__ u32x4 weight_tile[4 * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const uint32_t plane_bytes = (uint32_t)p.st_l * 2u;
+    const int L = p.l;
+
+    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+        const int tile = (int)(bu % tiles);
+        const int row_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
+        const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+        const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
+        const bool in_range = row_raw < p.n;
+        const int row = min(row_raw, p.n - 1);
+        int seen = 0;
+        const int slot = __builtin_amdgcn_readfirstlane(in_range ? route_ring_row(p, row, lane, &seen) : -2);
+        seen = __builtin_amdgcn_readfirstlane(seen);
+        const bool live = slot >= 0;
+
+        __builtin_amdgcn_s_setprio(3);
+        u32x4 wraw[kWeightChunks];
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        const Buffer sbuf = make_buffer(p.state + (int64_t)(live ? slot : 0) * p.st_s + c0,
+                                        live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+        u32x4 h[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            h[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)ring_pos(seen - 3 + k, L) + lane_off);
+        const u32x4 xv = buffer_load<kStream>(make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u),
+                                              lane_off);
+        __builtin_amdgcn_s_setprio(0);
+
+        float wf[32], bf[8];
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
+        const u32x4 y = conv8<ACT>(h[0], h[1], h[2], xv, wf, bf);
+        const u32x4 o = live ? y : u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
+
+        // stores after the taps are in registers: x overwrites the oldest token,
+        // which is tap 0 when L == 3
+        __builtin_amdgcn_sched_barrier(0);
+        buffer_store<kStream>(o, make_buffer(p.out + (int64_t)row * p.d + c0, in_range ? vec_bytes : 0u), lane_off);
+        buffer_store<kStream>(xv, sbuf, plane_bytes * (uint32_t)ring_pos(seen, L) + lane_off);
+        __syncthreads();  // the weight tile is reused by the next unit
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kScalarBlock) void update_ring_scalar(UpdateParams p, int tiles_per_row, int64_t units) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int row = (int)(unit / tiles_per_row);
+        const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
+        int seen = 0;
+        const int slot = route_ring_row(p, row, lane, &seen);
+        if (c >= p.d) continue;
+        uint16_t *o = p.out + (int64_t)row * p.d + c;
+        if (slot < 0) {
+            *o = 0;
+            continue;
+        }
+        const int L = p.l;
+        uint16_t *ring = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
+        const int64_t sl = p.st_l;
+        const uint16_t xb = p.x[(int64_t)row * p.ld + c];
+        const uint16_t *wt = p.weight + (int64_t)c * 4;
+        float acc = bf16_bits_to_f32(ring[ring_pos(seen - 3, L) * sl]) * bf16_bits_to_f32(wt[0]);
+        acc = __builtin_fmaf(bf16_bits_to_f32(ring[ring_pos(seen - 2, L) * sl]), bf16_bits_to_f32(wt[1]), acc);
+        acc = __builtin_fmaf(bf16_bits_to_f32(ring[ring_pos(seen - 1, L) * sl]), bf16_bits_to_f32(wt[2]), acc);
+        acc = __builtin_fmaf(bf16_bits_to_f32(xb), bf16_bits_to_f32(wt[3]), acc);
+        if (p.bias != nullptr) acc += bf16_bits_to_f32(p.bias[c]);
+        *o = f32_to_bf16_bits(activate<ACT>(acc));
+        ring[(int64_t)ring_pos(seen, L) * sl] = xb;
+    }
+}
+
+template <typename Kernel>
+hipError_t launch_ring(Kernel kernel, const UpdateParams &p, int tiles, int64_t units, int block,
+                       hipStream_t stream) {
+    const int64_t blocks = units < kMaxBlocks ? units : kMaxBlocks;
+    UpdateParams args_p = p;
+    int tiles_arg = tiles;
+    int64_t units_arg = units;
+    void *args[] = {&args_p, &tiles_arg, &units_arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(block), args, 0,
+                           stream);
+}
+
+}  // namespace
+
+hipError_t launch_update_ring(const UpdateParams &p, StateLayout layout, int activation, hipStream_t stream,
+                              const char **kernel_name) {
+    const bool silu = activation == DCCONV_ACT_SILU;
+    // Channel-last planes as 16-byte vectors, every descriptor below 2^30 bytes.
+    const bool v8 = layout == StateLayout::ChannelLast && p.d % kChPerLane == 0 && p.ld % kChPerLane == 0 &&
+                    p.st_s % kChPerLane == 0 && (int64_t)p.l * p.st_l * 2 + 2 * kChPerWave < ((int64_t)1 << 30);
+    if (v8) {
+        const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
+        const int64_t units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+        *kernel_name = silu ? "update_ring_v8<silu>" : "update_ring_v8<identity>";
+        if (p.bias != nullptr)
+            return silu ? launch_ring(update_ring_v8<DCCONV_ACT_SILU, true>, p, tiles, units, kBlock, stream)
+                        : launch_ring(update_ring_v8<DCCONV_ACT_IDENTITY, true>, p, tiles, units, kBlock, stream);
+        return silu ? launch_ring(update_ring_v8<DCCONV_ACT_SILU, false>, p, tiles, units, kBlock, stream)
+                    : launch_ring(update_ring_v8<DCCONV_ACT_IDENTITY, false>, p, tiles, units, kBlock, stream);
+    }
+    const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
+    const int64_t units = (int64_t)p.n * tiles;
+    *kernel_name = silu ? "update_ring_scalar<silu>" : "update_ring_scalar<identity>";
+    return silu ? launch_ring(update_ring_scalar<DCCONV_ACT_SILU>, p, tiles, units, kScalarBlock, stream)
+                : launch_ring(update_ring_scalar<DCCONV_ACT_IDENTITY>, p, tiles, units, kScalarBlock, stream);
+}
+
+}  // namespace dcconv

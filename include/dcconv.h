@@ -44,7 +44,7 @@ extern "C" {
 enum {
     DCCONV_OK = 0,
     DCCONV_EINVAL = 1,       /* contract violation: shape, stride, alignment, overlap, null */
-    DCCONV_EUNSUPPORTED = 2, /* semantically valid but not served (e.g. W != 4, cache_seqlens) */
+    DCCONV_EUNSUPPORTED = 2, /* semantically valid but not served (e.g. W != 4) */
     DCCONV_EHIP = 3          /* the HIP runtime refused the launch (hipGetLastError) */
 };
 
@@ -57,8 +57,9 @@ enum { DCCONV_ACT_IDENTITY = 0, DCCONV_ACT_SILU = 1 };
 enum {
     DCCONV_DEV_BAD_INDEX = 1, /* an index below -1, or not below S           */
     DCCONV_DEV_DUP_INDEX = 2, /* two rows of the batch select one real slot  */
-    DCCONV_DEV_BAD_SEQ = 4    /* dcconv_prefill: seq_starts is not 0 = starts[0]
+    DCCONV_DEV_BAD_SEQ = 4,   /* dcconv_prefill: seq_starts is not 0 = starts[0]
                                  <= starts[1] <= ... <= starts[n] = t          */
+    DCCONV_DEV_BAD_SEQLEN = 8 /* dcconv_update: a cache_seqlens entry below 0  */
 };
 
 /* The DCCONV_ABI_VERSION the library was built with. */
@@ -104,8 +105,17 @@ const char *dcconv_last_kernel(void);
  *             and DCCONV_DEV_DUP_INDEX is set; when dev_status is NULL duplicates
  *             are not detected and the result for the shared slot is unspecified
  *             (the page calls such an update "not transactional").
- * cache_seqlens  reserved; must be NULL, otherwise DCCONV_EUNSUPPORTED
- *             (the page raises NotImplementedError for anything but None).
+ * cache_seqlens  NULL, or int32 [n]: circular-buffer state, the use the page
+ *             reserves this keyword for (section "Causal Conv1d Decode Update").
+ *             c = cache_seqlens[r] is the number of tokens row r's slot has seen;
+ *             the slot keeps token i at position i mod l (k is then a ring
+ *             position, not an age).  The taps are tokens c-3, c-2, c-1, read at
+ *             positions (c-3+k) mod l before any write, and x; x then replaces
+ *             the oldest token at position c mod l, and no other value moves
+ *             (one element per channel is written).  cache_seqlens is only read
+ *             (the caller advances it).  An entry below 0 makes the row behave
+ *             as padding and sets DCCONV_DEV_BAD_SEQLEN.  Read-only; 4-byte
+ *             aligned; must not overlap anything the call writes.
  * activation  DCCONV_ACT_IDENTITY or DCCONV_ACT_SILU (SiLU(v) = v / (1 + e^-v)).
  * out         BF16 [n, d] contiguous, written.  Must not overlap any operand.
  * dev_status  NULL, or a device int32 the kernel ORs DCCONV_DEV_* bits into.
@@ -143,7 +153,9 @@ int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
  * n, d, t     rows, channels, tokens (t == 0 or n == 0: DCCONV_OK, nothing enqueued).
  * out         BF16, element (r, c, t) at out[r*os_n + c*os_d + t*os_t]; the strides
  *             must give every element its own address (no two (r, c, t) alias).
- * conv_state, s, l, st_*, weight, w, bias, conv_state_indices, cache_seqlens,
+ * cache_seqlens must be NULL here (circular-buffer state is served by
+ * dcconv_update only; DCCONV_EUNSUPPORTED otherwise).
+ * conv_state, s, l, st_*, weight, w, bias, conv_state_indices,
  * activation, dev_status, stream: exactly as for dcconv_update (the routing of a
  * row is the same for all of its tokens; a padding or rejected row writes zeros
  * for every token and leaves the state untouched).

@@ -93,7 +93,8 @@ DECLINES = [
     (dict(ld_x=70), dc.DCCONV_EINVAL, "ld_x % 8 == 0"),
     (dict(activation=2), dc.DCCONV_EINVAL, "activation"),
     (dict(st_d=-3), dc.DCCONV_EINVAL, "non-negative"),
-    (dict(cache_seqlens=IX), dc.DCCONV_EUNSUPPORTED, "cache_seqlens"),
+    (dict(cache_seqlens=IX + 2), dc.DCCONV_EINVAL, "cache_seqlens must be 4-byte aligned"),
+    (dict(cache_seqlens=OUT + 64), dc.DCCONV_EINVAL, "overlaps cache_seqlens"),
     (dict(w=3), dc.DCCONV_EUNSUPPORTED, "w=4"),
     (dict(w=5, l=4, st_d=4, st_s=256), dc.DCCONV_EUNSUPPORTED, "w=4"),
     (dict(st_s=192, st_d=1, st_l=2), dc.DCCONV_EUNSUPPORTED, "neither compact"),
@@ -164,10 +165,12 @@ def _cpu_args(N=4, D=16, L=3, S=4):
     return (torch.zeros(N, D, dtype=bf), torch.zeros(S, D, L, dtype=bf), torch.zeros(D, 4, dtype=bf))
 
 
-def test_frontend_refuses_cache_seqlens():
+def test_frontend_checks_cache_seqlens():
     x, st, w = _cpu_args()
-    with pytest.raises(NotImplementedError, match="cache_seqlens"):
-        dc.causal_conv1d_update(x, st, w, cache_seqlens=torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        dc.causal_conv1d_update(x, st, w, cache_seqlens=torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        dc.causal_conv1d_update(x, st, w, cache_seqlens=torch.zeros(3, dtype=torch.int32))
 
 
 def test_frontend_refuses_multi_token_x():

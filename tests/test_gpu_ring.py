@@ -1,0 +1,203 @@
+"""GPU parity of the decode step on circular-buffer state (``cache_seqlens``).
+
+The cuDNN FE-OSS page "Causal Conv1d Decode Update" reserves ``cache_seqlens``
+for circular-buffer state (section "Causal Conv1d Decode Update").  Ring
+reading: a slot that has seen c tokens keeps token i at position i mod L; the
+taps are tokens c-3..c-1 and x, and x replaces the oldest token at c mod L.
+Every case runs the HIP library and the CPU oracle on the same seeded inputs
+and requires the whole state buffer bit-exact (one value per channel written,
+guard bands intact), padding and rejected rows zero, and outputs within 1 BF16
+ulp or 1e-2 * max(1, |ref|) of the FP32 oracle (exact for identity).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import depthwise_causal_conv1d_amd as dc
+from depthwise_causal_conv1d_amd import workloads as wl
+from parity import (GUARD, assert_guards_intact, assert_outputs_match, from_dev, guarded_copy, guarded_empty,
+                    to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dc._load()
+    yield
+
+
+def _bf(rng, shape, scale=1.0):
+    return wl.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+class RingCase:
+    def __init__(self, seed, N, D, L, *, S=None, ld=None, layout="channel_last", bias=False, act="silu",
+                 routing="none", n_pad=0, max_seen=100, status=False):
+        rng = np.random.default_rng(seed)
+        self.N, self.D, self.L = N, D, L
+        self.S = N if S is None else S
+        self.ld = D if ld is None else ld
+        self.layout, self.act, self.status = layout, act, status
+        self.x = np.full((N, self.ld), wl.PAD_SENTINEL, np.uint16)
+        self.x[:, :D] = _bf(rng, (N, D))
+        self.weight = _bf(rng, (D, 4))
+        self.bias = _bf(rng, (D,), 0.1) if bias else None
+        if layout == "compact":
+            self.state0, self.st = _bf(rng, (self.S, D, L)), (D * L, L, 1)
+        else:
+            self.state0, self.st = _bf(rng, (self.S, L, D)), (L * D, 1, D)
+        self.indices = None
+        if routing == "unique":
+            self.indices = rng.choice(self.S, N, replace=False).astype(np.int32)
+        elif routing == "padded":
+            real = rng.choice(self.S, N - n_pad, replace=False).astype(np.int32)
+            self.indices = np.concatenate([real, np.full(n_pad, -1, np.int32)])[rng.permutation(N)].astype(np.int32)
+        self.oracle_indices = self.indices
+        seen = rng.integers(0, max_seen + 1, size=N).astype(np.int32)
+        seen[: min(N, 3)] = np.arange(min(N, 3))          # always cover c = 0, 1, 2 (window wraps)
+        self.seqlens = seen
+        self.oracle_seqlens = seen
+
+    def reference(self):
+        st = self.state0.copy()
+        out, out32 = oracle.update_ring(self.x, self.N, self.D, self.ld, st, self.S, self.L, self.st, self.weight,
+                                        self.bias, self.oracle_indices, self.oracle_seqlens, self.act, want_f32=True)
+        return out, out32, st
+
+    def run_gpu(self, dev="cuda"):
+        xb, xd = guarded_copy(self.x, dev)
+        sb, sd = guarded_copy(self.state0, dev)
+        sv = sd if self.layout == "compact" else sd.permute(0, 2, 1)
+        ob, od = guarded_empty((self.N, self.D), dev)
+        idd = None if self.indices is None else torch.from_numpy(self.indices).to(dev)
+        csd = torch.from_numpy(self.seqlens).to(dev)
+        stat = torch.zeros(1, dtype=torch.int32, device=dev) if self.status else None
+        dc.causal_conv1d_update_out(xd[:, :self.D], sv, to_dev(self.weight, dev),
+                                    None if self.bias is None else to_dev(self.bias, dev), self.act, out=od,
+                                    cache_seqlens=csd, conv_state_indices=idd, dev_status=stat)
+        self.kernel = dc.dcconv_last_kernel()
+        torch.cuda.synchronize()
+        assert_guards_intact(sb)
+        assert_guards_intact(ob)
+        assert np.array_equal(from_dev(xb)[GUARD:GUARD + self.x.size].reshape(self.x.shape), self.x)
+        np.testing.assert_array_equal(csd.cpu().numpy(), self.seqlens, err_msg="cache_seqlens was written")
+        return from_dev(od), from_dev(sd), (int(stat.item()) if stat is not None else None)
+
+    def check(self):
+        ref_out, ref32, ref_state = self.reference()
+        out, state, status = self.run_gpu()
+        np.testing.assert_array_equal(state, ref_state, err_msg="state not bit-exact")
+        assert_outputs_match(out, ref_out, ref32, exact=self.act in (None, "identity"))
+        if self.oracle_indices is not None:
+            assert np.all(wl.bf16_bits_to_f32(out[self.oracle_indices == -1]) == 0)
+        return status
+
+
+@pytest.mark.parametrize("L", [3, 4, 5, 8, 11])
+@pytest.mark.parametrize("act", [None, "silu"])
+def test_ring_channel_last(L, act):
+    case = RingCase(3000 + L, N=9, D=1096, L=L, bias=L % 2 == 1, act=act, routing="unique", S=13, ld=1104)
+    case.check()
+    assert case.kernel.startswith("update_ring_v8<"), case.kernel
+
+
+@pytest.mark.parametrize("L", [3, 4, 8])
+def test_ring_compact_takes_the_scalar_kernel(L):
+    case = RingCase(3100 + L, N=6, D=520, L=L, layout="compact", bias=True)
+    case.check()
+    assert case.kernel == "update_ring_scalar<silu>", case.kernel
+
+
+def test_ring_odd_channels_scalar():
+    case = RingCase(3150, N=5, D=37, L=4, layout="channel_last", act=None)
+    case.check()
+    assert case.kernel == "update_ring_scalar<identity>", case.kernel
+
+
+def test_ring_padding_bad_and_duplicate_rows():
+    case = RingCase(3200, N=10, D=1024, L=3, S=12, routing="padded", n_pad=2, status=True)
+    case.indices = case.indices.copy()
+    live = np.flatnonzero(case.indices >= 0)
+    case.indices[live[1]] = case.indices[live[4]]      # duplicate
+    case.indices[live[6]] = 12                         # out of range
+    case.seqlens = case.seqlens.copy()
+    case.seqlens[live[7]] = -5                         # negative count
+    oi = case.indices.copy()
+    oi[[live[1], live[4], live[6], live[7]]] = -1
+    case.oracle_indices = oi
+    cs = case.seqlens.copy(); cs[live[7]] = 0          # the oracle refuses negatives; the row is padding anyway
+    case.oracle_seqlens = cs
+    status = case.check()
+    assert status == dc.DCCONV_DEV_BAD_INDEX | dc.DCCONV_DEV_DUP_INDEX | dc.DCCONV_DEV_BAD_SEQLEN
+
+
+def test_ring_full_size_large_decode():
+    """The large decode batch (N=256, D=8192, L=3, SiLU, x row stride 8200) on a
+    channel-last ring, element by element."""
+    case = RingCase(3300, N=256, D=8192, L=3, ld=8200, max_seen=100000)
+    case.check()
+    assert case.kernel == "update_ring_v8<silu>"
+
+
+def test_ring_steps_equal_shifting_steps_on_gpu():
+    """Caller advances cache_seqlens each step; outputs equal the shifting update
+    on a linear copy of the same history, and the ring rotated by c equals it."""
+    rng = np.random.default_rng(3400)
+    N, D, L, T = 16, 2048, 4, 9
+    lin = _bf(rng, (N, L, D))                          # channel-last, position k = age order
+    c = rng.integers(0, 40, size=N).astype(np.int32)
+    ring = lin.copy()
+    for n in range(N):
+        for k in range(L):
+            ring[n, (c[n] + k) % L] = lin[n, k]
+    w, b = to_dev(_bf(rng, (D, 4))), to_dev(_bf(rng, (D,), 0.1))
+    ld, rd = to_dev(lin), to_dev(ring)
+    cd = torch.from_numpy(c).cuda()
+    for t in range(T):
+        xd = to_dev(_bf(rng, (N, D)))
+        o_lin = dc.causal_conv1d_update(xd, ld.permute(0, 2, 1), w, b, "silu")
+        o_ring = dc.causal_conv1d_update(xd, rd.permute(0, 2, 1), w, b, "silu", cache_seqlens=cd)
+        cd += 1
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(from_dev(o_ring), from_dev(o_lin))
+    lin_h, ring_h, c_h = from_dev(ld), from_dev(rd), cd.cpu().numpy()
+    for n in range(N):
+        for k in range(L):
+            np.testing.assert_array_equal(ring_h[n, (c_h[n] + k) % L], lin_h[n, k])
+
+
+def test_ring_in_hip_graph_with_advancing_counts():
+    """One graph holds the ring update and the counter increment; every replay
+    matches the oracle stepping the same way."""
+    rng = np.random.default_rng(3500)
+    N, D, L = 32, 1024, 3
+    st_h = _bf(rng, (N, L, D)); w_h = _bf(rng, (D, 4)); c_h = rng.integers(0, 10, size=N).astype(np.int32)
+    sd, wd = to_dev(st_h), to_dev(w_h)
+    cd = torch.from_numpy(c_h.copy()).cuda()
+    xd = torch.empty(N, D, dtype=torch.bfloat16, device="cuda")
+    od = torch.empty(N, D, dtype=torch.bfloat16, device="cuda")
+    xd.copy_(to_dev(_bf(rng, (N, D))))
+    dc.causal_conv1d_update_out(xd, sd.permute(0, 2, 1), wd, None, "silu", out=od, cache_seqlens=cd)  # warm
+    torch.cuda.synchronize()
+    st_h = from_dev(sd); c_h = cd.cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dc.causal_conv1d_update_out(xd, sd.permute(0, 2, 1), wd, None, "silu", out=od, cache_seqlens=cd)
+        cd.add_(1)
+    ref_state = np.ascontiguousarray(st_h.transpose(0, 2, 1))   # oracle in compact order
+    for step in range(4):
+        x_h = _bf(rng, (N, D))
+        xd.copy_(to_dev(x_h))
+        g.replay()
+        torch.cuda.synchronize()
+        ref, ref32 = oracle.update_ring(x_h, N, D, D, ref_state, N, L, (D * L, L, 1), w_h, None, None, c_h, "silu",
+                                        want_f32=True)
+        c_h = c_h + 1
+        assert_outputs_match(from_dev(od), ref, ref32, what=f"replay {step}")
+        np.testing.assert_array_equal(from_dev(sd), ref_state.transpose(0, 2, 1))
+        np.testing.assert_array_equal(cd.cpu().numpy(), c_h)
+        _ = (xd.float() * 2).sum().item()  # eager work between replays

@@ -317,8 +317,8 @@ def test_refusals_on_device_tensors():
     w = torch.zeros(64, 4, dtype=torch.bfloat16, device=dev)
     with pytest.raises(NotImplementedError):
         dc.causal_conv1d_update(x, st, torch.zeros(64, 3, dtype=torch.bfloat16, device=dev))
-    with pytest.raises(NotImplementedError):
-        dc.causal_conv1d_update(x, st, w, cache_seqlens=torch.zeros(4, dtype=torch.int32, device=dev))
+    with pytest.raises(ValueError):
+        dc.causal_conv1d_update(x, st, w, cache_seqlens=torch.zeros(4, dtype=torch.int64, device=dev))
     with pytest.raises(ValueError):
         dc.causal_conv1d_update(x, st[:3], w)            # S < N without a table
     with pytest.raises(ValueError):
