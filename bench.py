@@ -47,7 +47,8 @@ def kernel_source_hash(kernel: str) -> str:
     """Hash of the sources a kernel is compiled from (its file and the shared
     device helpers), so stale counter summaries are recognised."""
     main = ("update_tokens.hip" if kernel.startswith("tokens_") else
-            "prefill.hip" if kernel.startswith("prefill_") else "update.hip")
+            "prefill.hip" if kernel.startswith("prefill_") else
+            "update_ring.hip" if kernel.startswith("update_ring") else "update.hip")
     h = hashlib.sha256()
     for name in (main, "device_common.h"):
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -97,6 +98,7 @@ class Workload:
         self.sets = []
         x_all = up(data["x"])  # [T, N, ld]
         idx = None if data["indices"] is None else torch.from_numpy(data["indices"]).to(dev)
+        self.seqlens = None if data.get("seqlens") is None else torch.from_numpy(data["seqlens"]).to(dev)
         for i in range(self.n_sets):
             st = up(data["state"])
             if spec.layout == "channel_last":
@@ -112,7 +114,7 @@ class Workload:
         active = spec.N if data["indices"] is None else int((data["indices"] >= 0).sum())
         self.bytes_per_call = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active,
                                                    data["bias"] is not None, data["indices"] is not None,
-                                                   spec.layout, self.tokens)
+                                                   spec.layout, self.tokens, spec.ring)
 
     def step(self, i: int):
         import depthwise_causal_conv1d_amd as dc
@@ -127,7 +129,8 @@ class Workload:
             return
         t = (i // self.n_sets) % self.spec.T
         dc.causal_conv1d_update_out(s["x"][t, :, :D], s["state"], s["weight"], s["bias"],
-                                    self.spec.act, out=s["out"][:, 0, :], conv_state_indices=s["idx"])
+                                    self.spec.act, out=s["out"][:, 0, :], conv_state_indices=s["idx"],
+                                    cache_seqlens=self.seqlens)
 
 
 class PrefillWorkload:
@@ -250,7 +253,10 @@ def cpu_baseline(spec, host, seconds: float):
     while reps < 2 or t_total < seconds:
         st = host["state"].copy()
         t0 = time.perf_counter()
-        if tokens == 1:
+        if spec.ring:
+            oracle.update_ring(x, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
+                               host["weight"], host["bias"], host["indices"], host["seqlens"], spec.act)
+        elif tokens == 1:
             oracle.update_strided(x, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
                                   host["weight"], host["bias"], host["indices"], spec.act)
         else:
@@ -260,7 +266,7 @@ def cpu_baseline(spec, host, seconds: float):
         reps += 1
     active = spec.N if host["indices"] is None else int((host["indices"] >= 0).sum())
     b = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active, host["bias"] is not None,
-                             host["indices"] is not None, spec.layout, tokens)
+                             host["indices"] is not None, spec.layout, tokens, spec.ring)
     per_call = t_total / reps
     return {"value": b / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}, {tokens} token(s)) "

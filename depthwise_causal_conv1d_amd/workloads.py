@@ -45,6 +45,7 @@ class Spec:
     seed: int = 0
     layout: str = "compact"       # conv_state layout: "compact" [S, D, L] or "channel_last" [S, L, D]
     one_call: bool = False        # the T tokens go in one multi-token call (x viewed as [N, D, T])
+    ring: bool = False            # circular-buffer state: cache_seqlens drawn U{0..4095}
 
 
 # The five synthetic configurations.  Index 0 is the tiny case, 3 is the large
@@ -67,7 +68,8 @@ CONFIGS = [
 #
 # The multi-token form: the long-history workload's 16 steps as one call, and the
 # large decode batch advanced 4 tokens per call (as when several drafted tokens
-# are verified at once).
+# are verified at once).  And the large decode batch on a channel-last circular
+# buffer (cache_seqlens).
 EXTRA = [
     Spec("large_decode_channel_last", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
          routing="none", weight_dist="uniform", seed=4, layout="channel_last"),
@@ -75,6 +77,8 @@ EXTRA = [
          routing="unique", T=16, seed=5, one_call=True),
     Spec("large_decode_4tok", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
          routing="none", T=4, weight_dist="uniform", seed=4, one_call=True),
+    Spec("large_decode_ring", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
+         routing="none", weight_dist="uniform", seed=4, layout="channel_last", ring=True),
 ]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
@@ -96,7 +100,8 @@ def _normal(rng, shape, scale=1.0):
 
 
 def make(spec: Spec, seed: Optional[int] = None) -> dict:
-    """Draw one workload.  Order of draws: x, weight, conv_state, bias, indices.
+    """Draw one workload.  Order of draws: x, weight, conv_state, bias, indices,
+    cache_seqlens (ring workloads only).
 
     Returns a dict of host arrays:
       x        uint16 [T, N, ld] (T == 1 for one step); pad columns hold PAD_SENTINEL
@@ -104,6 +109,7 @@ def make(spec: Spec, seed: Optional[int] = None) -> dict:
       state    uint16 [S, D, L] (compact) or [S, L, D] (channel_last physical)
       bias     uint16 [D] or None
       indices  int32 [N] or None
+      seqlens  int32 [N] (ring workloads) or None
     """
     rng = np.random.default_rng(spec.seed if seed is None else seed)
     T, N, D, W, L, S, ld = spec.T, spec.N, spec.D, spec.W, spec.L, spec.S, spec.ld
@@ -129,7 +135,8 @@ def make(spec: Spec, seed: Optional[int] = None) -> dict:
         indices = rng.choice(S, N, replace=False).astype(np.int32)
     else:
         raise ValueError(spec.routing)
-    return {"x": x, "weight": weight, "state": state, "bias": bias, "indices": indices}
+    seqlens = rng.integers(0, 4096, size=N).astype(np.int32) if spec.ring else None
+    return {"x": x, "weight": weight, "state": state, "bias": bias, "indices": indices, "seqlens": seqlens}
 
 
 def state_strides(spec: Spec):
@@ -140,11 +147,14 @@ def state_strides(spec: Spec):
 
 
 def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bool,
-                      indices: bool, layout: str = "compact", tokens: int = 1) -> int:
+                      indices: bool, layout: str = "compact", tokens: int = 1, ring: bool = False) -> int:
     """Bytes one call that applies ``tokens`` decode steps must move at minimum:
     x of every token and the selected state read once, the state written back
     once (the history shifts, so all L values are rewritten), weight, bias, the
     output of every token, index table.  Padding rows read no x and no state.
+
+    With ``ring`` (circular-buffer state, one token) only the W-1 newest values
+    are read and one value per channel is written.
 
     State read: in the compact layout a channel's L values are adjacent, so all L
     are read.  Channel-last keeps each history position in its own plane; a
@@ -152,6 +162,11 @@ def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bo
     or survives into the final state (positions >= tokens), so
     L - min(tokens, L - (W-1)) planes are read (max(W-1, L-1) for one token)."""
     A, T = active_rows, tokens
+    if ring:
+        # circular buffer (one token): the W-1 newest values read, one value per
+        # channel written, plus the count table
+        return (2 * A * D + 2 * A * D * (W - 1) + 2 * A * D + 2 * D * W + (2 * D if bias else 0)
+                + 2 * N * D + (4 * N if indices else 0) + 4 * N)
     read_positions = L if layout == "compact" else L - min(T, L - (W - 1))
     return (2 * A * D * T + 2 * A * D * read_positions + 2 * A * D * L + 2 * D * W
             + (2 * D if bias else 0) + 2 * N * D * T + (4 * N if indices else 0))

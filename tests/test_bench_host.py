@@ -106,3 +106,18 @@ def test_cpu_baseline_prefill_leg():
     spec = wl.BY_NAME["prefill_varlen"]
     res = bench.cpu_baseline(spec, wl.make_prefill(spec), seconds=0.0)
     assert res["kind"] == "oracle" and res["value"] > 0 and "sequences" in res["sample"]
+
+
+def test_ring_bytes_by_hand():
+    # large decode batch on a ring: x, 3 newest values read, 1 written, out, weight, counts
+    N, D = 256, 8192
+    hand = 2 * N * D + 2 * N * D * 3 + 2 * N * D + 2 * N * D + 2 * D * 4 + 4 * N
+    assert wl.algorithmic_bytes(N, D, 4, 3, N, False, False, "channel_last", 1, ring=True) == hand
+
+
+def test_cpu_baseline_ring_leg():
+    spec = wl.BY_NAME["large_decode_ring"]
+    small = wl.Spec("ring_small", N=8, D=64, W=4, L=3, S=8, ld=64, bias=False, act="silu", routing="none",
+                    layout="channel_last", ring=True, seed=4)
+    res = bench.cpu_baseline(small, wl.make(small), seconds=0.0)
+    assert res["value"] > 0 and spec.ring
