@@ -8,10 +8,12 @@
 // Only one value per channel is written, instead of the L a shifting update
 // rewrites.
 //
-//  * update_ring_v8<ACT, HAS_BIAS>: channel-last state, where each position is a
-//    contiguous plane, so a row reads 3 planes and writes 1.  One wavefront per
-//    (row, 512-channel tile), 8 channels per lane; the block's two rows share
-//    the tile's weights.
+//  * update_ring_v8<ACT, R, HAS_BIAS>: channel-last state, where each position is
+//    a contiguous plane, so a row reads 3 planes and writes 1.  One wavefront
+//    per (R rows, 512-channel tile), 8 channels per lane, the block's waves
+//    sharing the tile's weights; every load is issued before the first row is
+//    computed and every store after the last (the structure of the shifting
+//    update's kernels).
 //  * update_ring_scalar<ACT>: one thread per (row, channel), any layout.
 #include <stdint.h>
 
@@ -43,7 +45,9 @@ __device__ __forceinline__ int route_ring_row(const UpdateParams &p, int row, in
     return slot;
 }
 
-template <int ACT, bool HAS_BIAS>
+// L3: the ring holds exactly the W-1 = 3 taps, so every plane is read whatever
+// the count, and the loads need not wait for it: tap k is plane (c + k) mod 3.
+template <int ACT, int R, bool HAS_BIAS, bool L3>
 __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int tiles, int64_t block_units) {
     __shared__ u32x4 weight_tile[4 * kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -52,46 +56,77 @@ __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int til
     const uint32_t plane_bytes = (uint32_t)p.st_l * 2u;
     const int L = p.l;
 
+    // A block owns one 512-channel tile and kWavesPerBlock groups of R rows.
     for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
         const int tile = (int)(bu % tiles);
-        const int row_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
+        const int group = (int)(bu / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
         const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
-        const bool in_range = row_raw < p.n;
-        const int row = min(row_raw, p.n - 1);
-        int seen = 0;
-        const int slot = __builtin_amdgcn_readfirstlane(in_range ? route_ring_row(p, row, lane, &seen) : -2);
-        seen = __builtin_amdgcn_readfirstlane(seen);
-        const bool live = slot >= 0;
 
+        int slot[R], head[R];  // head: ring position of the newest slot value + 1 (= c mod L)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = group * R + r;
+            int c = 0;
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_ring_row(p, row, lane, &c) : -2);
+            head[r] = __builtin_amdgcn_readfirstlane(c) % (L3 ? 3 : L);  // c >= 0 for a live row
+        }
+
+        // every load up front: weights, bias, then each row's x and tap planes
         __builtin_amdgcn_s_setprio(3);
         u32x4 wraw[kWeightChunks];
         weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
-        const Buffer sbuf = make_buffer(p.state + (int64_t)(live ? slot : 0) * p.st_s + c0,
-                                        live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
-        u32x4 h[3];
+        Buffer sbuf[R], obuf[R];
+        u32x4 h[R][3], xv[R];
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-            h[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)ring_pos(seen - 3 + k, L) + lane_off);
-        const u32x4 xv = buffer_load<kStream>(make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u),
-                                              lane_off);
+        for (int r = 0; r < R; ++r) {
+            const bool live = slot[r] >= 0;
+            const int row = min(group * R + r, p.n - 1);
+            sbuf[r] = make_buffer(p.state + (int64_t)(live ? slot[r] : 0) * p.st_s + c0,
+                                  live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+            obuf[r] = make_buffer(p.out + (int64_t)row * p.d + c0, slot[r] != -2 ? vec_bytes : 0u);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                // L3: plane k, placed below; else tap k's plane (c - 3 + k) mod L
+                const int pos = L3 ? k : (head[r] - 3 + k < 0 ? head[r] - 3 + k + L : head[r] - 3 + k);
+                h[r][k] = buffer_load<kStream>(sbuf[r], plane_bytes * (uint32_t)pos + lane_off);
+            }
+            xv[r] = buffer_load<kStream>(make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u), lane_off);
+        }
         __builtin_amdgcn_s_setprio(0);
+        if (L3) {
+            // tap k of row r is plane (c + k) mod 3: rotate the three planes by head
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const u32x4 p0 = h[r][0], p1 = h[r][1], p2 = h[r][2];
+                h[r][0] = head[r] == 0 ? p0 : head[r] == 1 ? p1 : p2;
+                h[r][1] = head[r] == 0 ? p1 : head[r] == 1 ? p2 : p0;
+                h[r][2] = head[r] == 0 ? p2 : head[r] == 1 ? p0 : p1;
+            }
+        }
 
         float wf[32], bf[8];
         weight_tile_share(weight_tile, wraw, wave, lane, wf);
         unpack_bias(bv, bf);
-        const u32x4 y = conv8<ACT>(h[0], h[1], h[2], xv, wf, bf);
-        const u32x4 o = live ? y : u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
+        u32x4 o[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 y = conv8<ACT>(h[r][0], h[r][1], h[r][2], xv[r], wf, bf);
+            o[r] = slot[r] >= 0 ? y : u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
+        }
 
-        // stores after the taps are in registers: x overwrites the oldest token,
-        // which is tap 0 when L == 3
+        // every store last, after the taps are in registers: x overwrites the
+        // oldest token, which is tap 0 when L == 3
         __builtin_amdgcn_sched_barrier(0);
-        buffer_store<kStream>(o, make_buffer(p.out + (int64_t)row * p.d + c0, in_range ? vec_bytes : 0u), lane_off);
-        buffer_store<kStream>(xv, sbuf, plane_bytes * (uint32_t)ring_pos(seen, L) + lane_off);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            buffer_store<kStream>(o[r], obuf[r], lane_off);
+            buffer_store<kStream>(xv[r], sbuf[r], plane_bytes * (uint32_t)head[r] + lane_off);
+        }
         __syncthreads();  // the weight tile is reused by the next unit
     }
 }
@@ -147,13 +182,30 @@ hipError_t launch_update_ring(const UpdateParams &p, StateLayout layout, int act
                     p.st_s % kChPerLane == 0 && (int64_t)p.l * p.st_l * 2 + 2 * kChPerWave < ((int64_t)1 << 30);
     if (v8) {
         const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
-        const int64_t units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
-        *kernel_name = silu ? "update_ring_v8<silu>" : "update_ring_v8<identity>";
-        if (p.bias != nullptr)
-            return silu ? launch_ring(update_ring_v8<DCCONV_ACT_SILU, true>, p, tiles, units, kBlock, stream)
-                        : launch_ring(update_ring_v8<DCCONV_ACT_IDENTITY, true>, p, tiles, units, kBlock, stream);
-        return silu ? launch_ring(update_ring_v8<DCCONV_ACT_SILU, false>, p, tiles, units, kBlock, stream)
-                    : launch_ring(update_ring_v8<DCCONV_ACT_IDENTITY, false>, p, tiles, units, kBlock, stream);
+        // two rows per wave once the grid still fills the chip with them
+        const bool two = ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
+        const int rows_per_block = kWavesPerBlock * (two ? 2 : 1);
+        const int64_t units = ((int64_t)p.n + rows_per_block - 1) / rows_per_block * tiles;
+        const bool l3 = p.l == 3;
+#define DCCONV_RING_GO(R_, B_, L3_)                                                                            \
+    return silu ? launch_ring(update_ring_v8<DCCONV_ACT_SILU, R_, B_, L3_>, p, tiles, units, kBlock, stream)    \
+                : launch_ring(update_ring_v8<DCCONV_ACT_IDENTITY, R_, B_, L3_>, p, tiles, units, kBlock, stream)
+#define DCCONV_RING_B(R_, L3_)              \
+    if (p.bias != nullptr) {                \
+        DCCONV_RING_GO(R_, true, L3_);      \
+    } else {                                \
+        DCCONV_RING_GO(R_, false, L3_);     \
+    }
+        if (two) {
+            *kernel_name = silu ? "update_ring_v8<silu,R=2>" : "update_ring_v8<identity,R=2>";
+            if (l3) { DCCONV_RING_B(2, true) }
+            DCCONV_RING_B(2, false)
+        }
+        *kernel_name = silu ? "update_ring_v8<silu,R=1>" : "update_ring_v8<identity,R=1>";
+        if (l3) { DCCONV_RING_B(1, true) }
+        DCCONV_RING_B(1, false)
+#undef DCCONV_RING_B
+#undef DCCONV_RING_GO
     }
     const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
     const int64_t units = (int64_t)p.n * tiles;

@@ -140,7 +140,7 @@ def test_ring_full_size_large_decode():
     channel-last ring, element by element."""
     case = RingCase(3300, N=256, D=8192, L=3, ld=8200, max_seen=100000)
     case.check()
-    assert case.kernel == "update_ring_v8<silu>"
+    assert case.kernel == "update_ring_v8<silu,R=2>", case.kernel
 
 
 def test_ring_steps_equal_shifting_steps_on_gpu():
