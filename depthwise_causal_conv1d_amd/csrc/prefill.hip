@@ -8,23 +8,27 @@
 //   out[i, c, j] = act(sum_k ext[L + j - 3 + k] * w[c, k] + bias[c])
 //   final state  = ext[T : T + L]
 //
-// Outputs j >= 3 depend on x alone, so they need no ordering at all:
-//  * prefill_chunks_v8<ACT, HAS_BIAS>: one wavefront per (512-channel tile,
-//    chunk of kChunk tokens), 8 channels per lane; the block's two waves take
-//    neighbouring chunks of one tile and share its weights.  A chunk re-reads
-//    the 3 tokens before it (its halo); blocks are mapped so that each XCD
-//    walks a contiguous run of chunks, where the halo is the neighbour's data
-//    and mostly hits that XCD's L2.  Tokens go in passes of 8, double
-//    buffered: the next pass's loads are issued before the current pass is
-//    computed and stored.
-//  * prefill_edges_v8<L, ACT, LAYOUT>: everything that touches a slot -- the
-//    first min(3, T) outputs, which read the initial state, and the final
-//    state, which replaces it -- one wavefront per (sequence, tile), so each
-//    slot is read and written by exactly one wave.
+// Outputs j >= 3 depend on x alone, so they need no ordering at all.  One
+// kernel, prefill_v8<L, ACT, layout, HAS_BIAS>, has two kinds of blocks:
+//  * chunk blocks: one wavefront per (512-channel tile,
+//    chunk of tokens), 8 channels per lane; the block's two waves take
+//    neighbouring chunks of one tile and share its weights.  The chunk length
+//    is set per call so that about 8 waves per CU each stream one long run (a
+//    single resident round; 128 tokens for 8 x 2048 tokens at D = 8192).  A
+//    chunk re-reads the 3 tokens before it (its halo); with short chunks the
+//    blocks are mapped so that each XCD walks a contiguous run of chunks, where
+//    the halo is the neighbour's data in that XCD's L2.  Tokens go in passes of
+//    4, double buffered: the next pass's loads are issued before the current
+//    pass is computed and stored.
+//  * edge blocks: everything that touches a slot -- the first min(3, T)
+//    outputs, which read the initial state, and the final state, which
+//    replaces it -- one wavefront per (sequence, tile), so each slot is read
+//    and written by exactly one wave.  They come first in the grid, so their
+//    short dependent chains run under the chunk blocks' streaming.
 //  * prefill_scalar<ACT>: one thread per (sequence, channel) walking its
 //    tokens in order; any strides, any L >= 3.
-// The edge and chunk kernels write disjoint outputs and read x only, so their
-// order on the stream does not matter; the edges go first.
+// The two roles write disjoint outputs and read x only, so they need no
+// ordering between them.
 #include <stdint.h>
 
 #include "dcconv.h"
@@ -34,8 +38,13 @@
 namespace dcconv {
 namespace {
 
-constexpr int kChunk = 32;  // tokens per wave unit of the chunk kernel
-constexpr int kPass = 8;    // tokens per load pass
+// Tokens per wave unit of the chunk kernel: chosen per call so that the grid
+// holds about kTargetWaves waves (8 per CU: one resident round at this kernel's
+// register use), within [kMinChunk, kMaxChunk] and a multiple of kPass.
+constexpr int kMinChunk = 16;
+constexpr int kMaxChunk = 256;
+constexpr int64_t kTargetWaves = 2048;
+constexpr int kPass = 4;    // tokens per load pass
 constexpr int kXcds = 8;    // MI355X: workgroups go round-robin over 8 XCDs
 // Buffer offsets beyond every descriptor used here (all are below 2^30 bytes):
 // a token outside the piece, and a lane past a ragged tile.  Their sum and any
@@ -103,19 +112,20 @@ __device__ __forceinline__ void chunk_piece(const PrefillParams &p, int i, int j
     }
 }
 
+// One block of the chunk role: virtual block vb of v_blocks (a multiple of 8).
 template <int ACT, bool HAS_BIAS>
-__global__ __launch_bounds__(kBlock) void prefill_chunks_v8(PrefillParams p, int tiles, int64_t units,
-                                                            int64_t units_per_seq, int64_t n_blocks,
-                                                            int64_t v_blocks) {
-    __shared__ u32x4 weight_tile[4 * kWave];
+__device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weight_tile, int tiles, int chunk,
+                                            int xcd_map, int64_t units, int64_t units_per_seq, int64_t n_blocks,
+                                            int64_t v_blocks, int64_t vb) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const int64_t per_xcd = v_blocks / kXcds;
-    for (int64_t vb = blockIdx.x; vb < v_blocks; vb += gridDim.x) {
-        // workgroup vb runs on XCD vb % 8: give each XCD a contiguous run of blocks
-        const int64_t v = (vb % kXcds) * per_xcd + vb / kXcds;
-        if (v >= n_blocks) continue;  // block-uniform
+    {
+        // workgroup vb runs on XCD vb % 8: with short chunks give each XCD a
+        // contiguous run of blocks (their halos are each other's data)
+        const int64_t v = xcd_map ? (vb % kXcds) * per_xcd + vb / kXcds : vb;
+        if (v >= n_blocks) return;  // block-uniform
         const int tile = (int)(v % tiles);
         const int64_t unit = (v / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -135,14 +145,14 @@ __global__ __launch_bounds__(kBlock) void prefill_chunks_v8(PrefillParams p, int
             if (p.starts == nullptr) {
                 // batch form: the unit is chunk c of sequence i
                 const int i = (int)(unit / units_per_seq);
-                const int j0 = (int)(unit % units_per_seq) * kChunk;
-                const int j1 = min(p.t, j0 + kChunk);
+                const int j0 = (int)(unit % units_per_seq) * chunk;
+                const int j1 = min(p.t, j0 + chunk);
                 chunk_piece<ACT>(p, i, j0, j1, p.x + (int64_t)i * p.xs_n, p.out + (int64_t)i * p.os_n, c0, vec_bytes,
                                  lane_off, lane, wf, bf);
             } else {
                 // packed form: the unit is packed tokens [q, q1), cut at sequence boundaries
-                int q = (int)unit * kChunk;
-                const int q1 = min(p.t, q + kChunk);
+                int q = (int)unit * chunk;
+                const int q1 = min(p.t, q + chunk);
                 int i = find_seq(p.starts, p.n, q);
                 while (q < q1) {  // each pass advances q or i; i is bounded by n
                     if (i < 0 || i >= p.n) break;
@@ -167,18 +177,18 @@ __global__ __launch_bounds__(kBlock) void prefill_chunks_v8(PrefillParams p, int
     }
 }
 
+// One block of the edge role: block unit bu = (pair of sequences, tile).
+// stage_all holds kWave * L vectors per wave: the compact state's
+// transposition, then the planes, which the final state picks at a run-time
+// position.
 template <int L, int ACT, int LAYOUT>
-__global__ __launch_bounds__(kBlock) void prefill_edges_v8(PrefillParams p, int tiles, int64_t block_units) {
-    // per wave: the compact state's transposition, then the planes, which the
-    // final state picks at a run-time position
-    __shared__ u32x4 stage_all[kWavesPerBlock][kWave * L];
-    __shared__ u32x4 weight_tile[4 * kWave];
+__device__ __forceinline__ void edge_block(const PrefillParams &p, u32x4 *stage_all, u32x4 *weight_tile, int tiles,
+                                           int64_t bu) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
-
-    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+    {
         const int tile = (int)(bu % tiles);
         const int i_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void prefill_edges_v8(PrefillParams p, int 
 
         u32x4 pl[L];
         if (LAYOUT == kCompactState) {
-            u32x4 *stage = stage_all[wave];
+            u32x4 *stage = stage_all + wave * (kWave * L);
 #pragma unroll
             for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[j];
             wave_lds_sync();
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void prefill_edges_v8(PrefillParams p, int 
         }
         // final state: position k is ext[len + k], a token or (len + k < L) the
         // initial plane len + k, picked through LDS (a run-time position)
-        u32x4 *stage = stage_all[wave];
+        u32x4 *stage = stage_all + wave * (kWave * L);
         wave_lds_sync();
 #pragma unroll
         for (int k = 0; k < L; ++k) stage[k * kWave + lane] = pl[k];
@@ -321,6 +331,26 @@ __global__ __launch_bounds__(kBlock) void prefill_edges_v8(PrefillParams p, int 
             for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[j], wbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
         }
         __syncthreads();  // the stage and the weight tile are reused by the next unit
+    }
+}
+
+// Both roles in one launch: the edge blocks first (they start before the long
+// chunk blocks and finish under them), then the chunk blocks.  edge_blocks is a
+// multiple of 8, so chunk block vb runs on XCD vb % 8.
+template <int L, int ACT, int LAYOUT, bool HAS_BIAS>
+__global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles, int chunk, int xcd_map,
+                                                     int64_t units, int64_t units_per_seq, int64_t n_blocks,
+                                                     int64_t v_blocks, int64_t edge_units, int64_t edge_blocks) {
+    __shared__ u32x4 stage_all[kWavesPerBlock * kWave * L];
+    __shared__ u32x4 weight_tile[4 * kWave];
+    const int64_t total = edge_blocks + v_blocks;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        if (b < edge_blocks) {
+            if (b < edge_units) edge_block<L, ACT, LAYOUT>(p, stage_all, weight_tile, tiles, b);
+        } else {
+            chunk_block<ACT, HAS_BIAS>(p, weight_tile, tiles, chunk, xcd_map, units, units_per_seq, n_blocks, v_blocks,
+                                       b - edge_blocks);
+        }
     }
 }
 
@@ -396,57 +426,56 @@ hipError_t launch(Kernel kernel, int64_t blocks, int block, hipStream_t stream, 
                            stream);
 }
 
-template <int ACT>
-hipError_t launch_chunks(const PrefillParams &p, int tiles, hipStream_t stream) {
-    const int64_t units_per_seq = ((int64_t)p.t + kChunk - 1) / kChunk;
+template <int L, int ACT, int LAYOUT>
+hipError_t launch_prefill_l(const PrefillParams &p, int tiles, hipStream_t stream) {
+    const int64_t tokens = p.starts != nullptr ? (int64_t)p.t : (int64_t)p.t * p.n;
+    int64_t chunk = (tokens * tiles + kTargetWaves - 1) / kTargetWaves;
+    chunk = (chunk + kPass - 1) / kPass * kPass;
+    chunk = chunk < kMinChunk ? kMinChunk : chunk > kMaxChunk ? kMaxChunk : chunk;
+    const int64_t units_per_seq = ((int64_t)p.t + chunk - 1) / chunk;
     const int64_t units = p.starts != nullptr ? units_per_seq : units_per_seq * p.n;
-    if (units == 0) return hipSuccess;
+    const int xcd_map = chunk < 64;
     const int64_t n_blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
     const int64_t v_blocks = (n_blocks + kXcds - 1) / kXcds * kXcds;
-    const int64_t grid = v_blocks < kMaxBlocks ? v_blocks : kMaxBlocks;  // kMaxBlocks is a multiple of 8
+    const int64_t edge_units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+    const int64_t edge_blocks = (edge_units + kXcds - 1) / kXcds * kXcds;
+    const int64_t total = edge_blocks + v_blocks;
+    const int64_t grid = total < kMaxBlocks ? total : kMaxBlocks;  // both multiples of 8
     PrefillParams pp = p;
+    const int ch = (int)chunk;
     return p.bias != nullptr
-               ? launch(prefill_chunks_v8<ACT, true>, grid, kBlock, stream, pp, tiles, units, units_per_seq, n_blocks,
-                        v_blocks)
-               : launch(prefill_chunks_v8<ACT, false>, grid, kBlock, stream, pp, tiles, units, units_per_seq,
-                        n_blocks, v_blocks);
-}
-
-template <int L, int ACT, int LAYOUT>
-hipError_t launch_edges(const PrefillParams &p, int tiles, hipStream_t stream) {
-    const int64_t block_units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
-    const int64_t grid = block_units < kMaxBlocks ? block_units : kMaxBlocks;
-    PrefillParams pp = p;
-    return launch(prefill_edges_v8<L, ACT, LAYOUT>, grid, kBlock, stream, pp, tiles, block_units);
+               ? launch(prefill_v8<L, ACT, LAYOUT, true>, grid, kBlock, stream, pp, tiles, ch, xcd_map, units,
+                        units_per_seq, n_blocks, v_blocks, edge_units, edge_blocks)
+               : launch(prefill_v8<L, ACT, LAYOUT, false>, grid, kBlock, stream, pp, tiles, ch, xcd_map, units,
+                        units_per_seq, n_blocks, v_blocks, edge_units, edge_blocks);
 }
 
 template <int ACT, int LAYOUT>
-hipError_t launch_edges_l(const PrefillParams &p, int tiles, hipStream_t stream, const char **name) {
-#define DCCONV_PF_NAME(LL)                                                                                        \
-    (LAYOUT == kStateless                                                                                         \
-         ? (ACT ? "prefill_edges_v8<stateless,silu>+prefill_chunks_v8<silu>"                                      \
-                : "prefill_edges_v8<stateless,identity>+prefill_chunks_v8<identity>")                             \
-         : LAYOUT == kCompactState                                                                                \
-               ? (ACT ? "prefill_edges_v8<L=" #LL ",silu,compact>+prefill_chunks_v8<silu>"                        \
-                      : "prefill_edges_v8<L=" #LL ",identity,compact>+prefill_chunks_v8<identity>")               \
-               : (ACT ? "prefill_edges_v8<L=" #LL ",silu,channel_last>+prefill_chunks_v8<silu>"                   \
-                      : "prefill_edges_v8<L=" #LL ",identity,channel_last>+prefill_chunks_v8<identity>"))
-#define DCCONV_PF_CASE(LL)                                 \
-    case LL:                                               \
-        *name = DCCONV_PF_NAME(LL);                        \
-        return launch_edges<LL, ACT, LAYOUT>(p, tiles, stream);
-    if (LAYOUT == kStateless) {
+hipError_t launch_prefill_layout(const PrefillParams &p, int tiles, hipStream_t stream, const char **name) {
+#define DCCONV_PF_NAME(LL)                                                                              \
+    (LAYOUT == kStateless                                                                               \
+         ? (ACT ? "prefill_v8<stateless,silu>" : "prefill_v8<stateless,identity>")                      \
+         : LAYOUT == kCompactState                                                                      \
+               ? (ACT ? "prefill_v8<L=" #LL ",silu,compact>" : "prefill_v8<L=" #LL ",identity,compact>") \
+               : (ACT ? "prefill_v8<L=" #LL ",silu,channel_last>"                                       \
+                      : "prefill_v8<L=" #LL ",identity,channel_last>"))
+#define DCCONV_PF_CASE(LL)          \
+    case LL:                        \
+        *name = DCCONV_PF_NAME(LL); \
+        return launch_prefill_l<LL, ACT, LAYOUT>(p, tiles, stream);
+    if constexpr (LAYOUT == kStateless) {
         *name = DCCONV_PF_NAME(3);
-        return launch_edges<3, ACT, kStateless>(p, tiles, stream);
-    }
-    switch (p.l) {
-        DCCONV_PF_CASE(3)
-        DCCONV_PF_CASE(4)
-        DCCONV_PF_CASE(5)
-        DCCONV_PF_CASE(6)
-        DCCONV_PF_CASE(7)
-        DCCONV_PF_CASE(8)
-        default: return hipErrorInvalidValue;
+        return launch_prefill_l<3, ACT, kStateless>(p, tiles, stream);
+    } else {
+        switch (p.l) {
+            DCCONV_PF_CASE(3)
+            DCCONV_PF_CASE(4)
+            DCCONV_PF_CASE(5)
+            DCCONV_PF_CASE(6)
+            DCCONV_PF_CASE(7)
+            DCCONV_PF_CASE(8)
+            default: return hipErrorInvalidValue;
+        }
     }
 #undef DCCONV_PF_CASE
 #undef DCCONV_PF_NAME
@@ -455,15 +484,9 @@ hipError_t launch_edges_l(const PrefillParams &p, int tiles, hipStream_t stream,
 template <int ACT>
 hipError_t launch_prefill_v8(const PrefillParams &p, StateLayout layout, hipStream_t stream, const char **name) {
     const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
-    hipError_t err;
-    if (p.state == nullptr)
-        err = launch_edges_l<ACT, kStateless>(p, tiles, stream, name);
-    else if (layout == StateLayout::ChannelLast)
-        err = launch_edges_l<ACT, kChannelLastState>(p, tiles, stream, name);
-    else
-        err = launch_edges_l<ACT, kCompactState>(p, tiles, stream, name);
-    if (err != hipSuccess) return err;
-    return launch_chunks<ACT>(p, tiles, stream);
+    if (p.state == nullptr) return launch_prefill_layout<ACT, kStateless>(p, tiles, stream, name);
+    if (layout == StateLayout::ChannelLast) return launch_prefill_layout<ACT, kChannelLastState>(p, tiles, stream, name);
+    return launch_prefill_layout<ACT, kCompactState>(p, tiles, stream, name);
 }
 
 }  // namespace
@@ -478,8 +501,8 @@ hipError_t launch_prefill(const PrefillParams &p, StateLayout layout, int activa
     // halo, the 3 head or L tail tokens of the edges, the L state planes.
     const bool v8 = p.d % kChPerLane == 0 && p.xs_d == 1 && p.os_d == 1 && p.xs_t % 8 == 0 && p.os_t % 8 == 0 &&
                     (p.starts != nullptr || p.n == 1 || (p.xs_n % 8 == 0 && p.os_n % 8 == 0)) &&
-                    p.xs_t * 2 * (int64_t)(kChunk + 3) + 2 * kChPerWave < lim &&
-                    p.os_t * 2 * (int64_t)(kChunk + 3) + 2 * kChPerWave < lim &&
+                    p.xs_t * 2 * (int64_t)(kMaxChunk + 3) + 2 * kChPerWave < lim &&
+                    p.os_t * 2 * (int64_t)(kMaxChunk + 3) + 2 * kChPerWave < lim &&
                     (!stateful || (p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8 &&
                                    p.st_l * 2 * (int64_t)p.l + 2 * kChPerWave < lim));
     if (v8) return silu ? launch_prefill_v8<DCCONV_ACT_SILU>(p, layout, stream, kernel_name)

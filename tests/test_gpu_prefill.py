@@ -137,7 +137,7 @@ def test_prefill_batch_compact(L, T):
     case = PrefillCase(2000 + 10 * L + T, 1096, N=3, T=T, L=L, state="compact", bias=T % 2 == 0,
                        act=None if T % 3 == 0 else "silu")
     case.check()
-    assert case.kernel.startswith(f"prefill_edges_v8<L={L},") and "compact" in case.kernel, case.kernel
+    assert case.kernel == f"prefill_v8<L={L},{'identity' if T % 3 == 0 else 'silu'},compact>", case.kernel
 
 
 @pytest.mark.parametrize("L", [3, 5, 6, 7, 8])
@@ -153,7 +153,7 @@ def test_prefill_batch_channel_last(L, T):
 def test_prefill_stateless(T):
     case = PrefillCase(2200 + T, 520, N=4, T=T, state=None, bias=True)
     case.check()
-    assert case.kernel.startswith("prefill_edges_v8<stateless,silu>"), case.kernel
+    assert case.kernel == "prefill_v8<stateless,silu>", case.kernel
 
 
 def test_prefill_zero_tokens_writes_final_states():
@@ -296,3 +296,19 @@ def test_prefill_full_size(layout):
     case = PrefillCase(2700, 4096, N=2, T=2048, L=3, state=layout, has_init="mixed", act="silu")
     case.check()
     assert f"L=3,silu,{layout}" in case.kernel, case.kernel
+
+
+@pytest.mark.parametrize("T", [200_000, 524_288])
+def test_prefill_long_chunks(T):
+    """A long sequence at a narrow width: the chunk kernel's per-call chunk
+    length grows to its largest values (about 100 and 256 tokens per wave)."""
+    case = PrefillCase(2800 + T % 97, 64, N=1, T=T, L=3, state="channel_last", has_init="all", bias=True)
+    case.check()
+
+
+def test_prefill_packed_long_chunks_cross_many_sequences():
+    """Packed sequences shorter than a chunk: one wave's chunk spans many of them."""
+    rng = np.random.default_rng(2900)
+    lens = [int(v) for v in rng.integers(0, 40, size=3000)]
+    case = PrefillCase(2900, 64, lens=lens, L=4, state="compact", routing="unique", S=3000, has_init="mixed")
+    case.check()
