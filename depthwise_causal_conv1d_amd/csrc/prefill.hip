@@ -54,17 +54,24 @@ constexpr uint32_t kBadLane = 1u << 31;
 
 enum { kStateless = 0, kCompactState = 1, kChannelLastState = 2 };
 
-// Largest i in [0, n] with starts[i] <= p, or -1 (wave-uniform binary search).
-__device__ __forceinline__ int find_seq(const int32_t *starts, int n, int p) {
-    int lo = 0, hi = n + 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (starts[mid] <= p)
-            lo = mid + 1;
-        else
-            hi = mid;
+// Largest i in [0, n] with starts[i] <= q, or -1.  Each round the 64 lanes
+// probe 64 evenly spaced entries of the remaining range at once, so the search
+// costs ceil(log64(n + 1)) dependent loads instead of log2(n + 1).  All 64
+// lanes call it; the result is wave-uniform.  Any table (ordered or not)
+// narrows the range every round, so the loop ends.
+__device__ __forceinline__ int find_seq(const int32_t *starts, int n, int q, int lane) {
+    int lo = 0, hi = n;  // candidates lo..hi
+    for (;;) {
+        const int step = (hi - lo + kWave) / kWave;  // ceil((hi - lo + 1) / 64)
+        const int idx = lo + lane * step;
+        const bool le = idx <= hi && starts[idx] <= q;
+        const int below = __popcll(__ballot(le));  // probes <= q: a prefix of the lanes for an ordered table
+        if (below == 0) return lo - 1;
+        const int base = lo + (below - 1) * step;
+        if (step == 1) return base;
+        lo = base;
+        hi = min(hi, base + step - 1);
     }
-    return lo - 1;
 }
 
 // Outputs j in [max(j0, 3), j1) of sequence i, whose token j (channel c0 + ...)
@@ -73,10 +80,13 @@ template <int ACT>
 __device__ __forceinline__ void chunk_piece(const PrefillParams &p, int i, int j0, int j1, const uint16_t *xseq,
                                             uint16_t *oseq, int c0, uint32_t vec_bytes, uint32_t lane_off, int lane,
                                             const float (&wf)[32], const float (&bf)[8]) {
+    // The x loads do not wait for the routing: a padding sequence's tokens are
+    // read too (they are valid memory) and its outputs are then zeroed, which
+    // keeps the index load off the loads' dependence chain.
     const bool live = route_row(p.idx, p.status, p.n, p.s, i, lane) >= 0;
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u;
     const int jb = max(j0 - 3, 0);  // first token read: the halo, clipped at the sequence start
-    const Buffer xbuf = make_buffer(xseq + (int64_t)jb * p.xs_t + c0, live ? x_tok * (uint32_t)(j1 - 1 - jb) + vec_bytes : 0u);
+    const Buffer xbuf = make_buffer(xseq + (int64_t)jb * p.xs_t + c0, x_tok * (uint32_t)(j1 - 1 - jb) + vec_bytes);
     const Buffer obuf = make_buffer(oseq + (int64_t)j0 * p.os_t + c0, o_tok * (uint32_t)(j1 - 1 - j0) + vec_bytes);
     auto xoff = [&](int j) -> uint32_t {
         return ((j >= jb && j < j1) ? x_tok * (uint32_t)(j - jb) : kBadToken) + lane_off;
@@ -153,7 +163,7 @@ __device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weigh
                 // packed form: the unit is packed tokens [q, q1), cut at sequence boundaries
                 int q = (int)unit * chunk;
                 const int q1 = min(p.t, q + chunk);
-                int i = find_seq(p.starts, p.n, q);
+                int i = find_seq(p.starts, p.n, q, lane);
                 while (q < q1) {  // each pass advances q or i; i is bounded by n
                     if (i < 0 || i >= p.n) break;
                     const int a = p.starts[i], e = p.starts[i + 1];
