@@ -9,12 +9,13 @@
 // once instead of T times: per active channel-row the bytes drop from
 // T * (4 + 4L) + 2T to 4L + 4T (compact layout).
 //
-//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST>: one wavefront owns one row of one
-//    512-channel tile (8 channels per lane), the block shares the tile's weights.
+//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP>: one wavefront owns R rows
+//    of one 512-channel tile (8 channels per lane), the block shares the tile's
+//    weights.
 //    The history lives in registers in plane-major form (one 16-byte vector per
 //    history position, 8 channels each), so a token's shift is a renaming of
-//    registers.  Tokens go in passes of 8: the pass's x vectors are all loaded
-//    before the first is used and its 8 outputs are all stored after the last
+//    registers.  Tokens go in passes of KP: the pass's x vectors are all loaded
+//    before the first is used and its outputs are all stored after the last
 //    is computed.  Compact state goes through the same LDS stage as the
 //    single-token kernel; channel-last state is already plane-major.
 //  * tokens_scalar<ACT>: one thread per (row, channel), any strides, any L >= 3;
@@ -28,14 +29,13 @@
 namespace dcconv {
 namespace {
 
-constexpr int kTokensPerPass = 8;
 // Buffer offsets that lie beyond every descriptor (all descriptors used here are
 // smaller than 2^30 bytes): one for a token past the end, one for a lane past a
 // ragged tile.  Their sum stays below 2^32.
 constexpr uint32_t kBadToken = 1u << 30;
 constexpr uint32_t kBadLane = 1u << 31;
 
-template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST>
+template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP>
 __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_per_row, int64_t block_units) {
     __shared__ u32x4 stage_all[kWavesPerBlock][CHANNEL_LAST ? 1 : kWave * L];
     __shared__ u32x4 weight_tile[4 * kWave];
@@ -47,129 +47,145 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
 
+    // A block owns one 512-channel tile and kWavesPerBlock groups of R rows.
     for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
         const int tile = (int)(bu % tiles_per_row);
-        const int row_raw = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
+        const int group = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
         const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
-        const int slot = __builtin_amdgcn_readfirstlane(row_raw < p.n ? route_row(p.idx, p.status, p.n, p.s, row_raw, lane)
-                                                                       : -2);
-        const bool live = slot >= 0;
-        const int row = min(row_raw, p.n - 1);
+        int slot[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = group * R + r;
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p.idx, p.status, p.n, p.s, row, lane) : -2);
+        }
 
+        // every load of the first pass up front: weights, bias, each row's
+        // state and its first KP tokens
         __builtin_amdgcn_s_setprio(3);
         u32x4 wraw[kWeightChunks];
         weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
-        // State: compact = the tile's contiguous run of L KiB, read coalesced;
-        // channel-last = planes kFirst..L-1 of this tile.
-        Buffer sbuf;
-        u32x4 sv[L];
-        if (CHANNEL_LAST) {
-            sbuf = make_buffer(live ? p.state + (int64_t)slot * p.st_s + c0 : p.x,
-                               live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+        Buffer sbuf[R], xbuf[R], obuf[R];
+        u32x4 sv[R][L], xv[R][KP];
 #pragma unroll
-            for (int k = kFirst; k < L; ++k) sv[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)k + lane_off);
-        } else {
-            sbuf = make_buffer(live ? p.state + (int64_t)slot * p.st_s + (int64_t)c0 * L : p.x,
-                               live ? vec_bytes * L : 0u);
+        for (int r = 0; r < R; ++r) {
+            const bool live = slot[r] >= 0;
+            const int row = min(group * R + r, p.n - 1);
+            // State: compact = the tile's contiguous run of L KiB, read coalesced;
+            // channel-last = planes kFirst..L-1 of this tile.
+            if (CHANNEL_LAST) {
+                sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + c0 : p.x,
+                                      live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
 #pragma unroll
-            for (int j = 0; j < L; ++j) sv[j] = buffer_load<kStream>(sbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
+                for (int k = 0; k < L; ++k)
+                    sv[r][k] = k < kFirst ? u32x4{0u, 0u, 0u, 0u}
+                                          : buffer_load<kStream>(sbuf[r], plane_bytes * (uint32_t)k + lane_off);
+            } else {
+                sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + (int64_t)c0 * L : p.x,
+                                      live ? vec_bytes * L : 0u);
+#pragma unroll
+                for (int j = 0; j < L; ++j)
+                    sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+            }
+            // x and out of this row: one descriptor each, spanning every token
+            xbuf[r] = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+            obuf[r] = make_buffer(p.out + (int64_t)row * p.os_n + c0,
+                                  slot[r] != -2 ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+#pragma unroll
+            for (int i = 0; i < KP; ++i)
+                xv[r][i] = buffer_load<kStream>(xbuf[r], (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
         }
-        // x and out of this row: one descriptor each, spanning every token.
-        const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.xs_n + c0,
-                                        live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
-        const Buffer obuf = make_buffer(p.out + (int64_t)row * p.os_n + c0,
-                                        row_raw < p.n ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
-        u32x4 xv[kTokensPerPass];
-#pragma unroll
-        for (int i = 0; i < kTokensPerPass; ++i)
-            xv[i] = buffer_load<kStream>(xbuf, (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
         __builtin_amdgcn_s_setprio(0);
 
         float wf[32], bf[8];
         weight_tile_share(weight_tile, wraw, wave, lane, wf);
         unpack_bias(bv, bf);
 
-        u32x4 pl[L];
-        if (CHANNEL_LAST) {
+        u32x4 pl[R][L];
 #pragma unroll
-            for (int k = 0; k < L; ++k) pl[k] = k < kFirst ? u32x4{0u, 0u, 0u, 0u} : sv[k];
-        } else {
-            u32x4 *stage = stage_all[wave];
+        for (int r = 0; r < R; ++r) {
+            if (CHANNEL_LAST) {
 #pragma unroll
-            for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[j];
-            wave_lds_sync();
-            uint32_t h[4 * L];
+                for (int k = 0; k < L; ++k) pl[r][k] = sv[r][k];
+            } else {
+                u32x4 *stage = stage_all[wave];
+                wave_lds_sync();
 #pragma unroll
-            for (int k = 0; k < L; ++k) {
-                const u32x4 t = stage[lane * L + k];
+                for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[r][j];
+                wave_lds_sync();
+                uint32_t h[4 * L];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) h[4 * k + q] = t[q];
+                for (int k = 0; k < L; ++k) {
+                    const u32x4 t = stage[lane * L + k];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) h[4 * k + q] = t[q];
+                }
+                to_planes<L>(h, pl[r]);
             }
-            to_planes<L>(h, pl);
         }
 
-        for (int t0 = 0; t0 < p.t; t0 += kTokensPerPass) {
+        for (int t0 = 0; t0 < p.t; t0 += KP) {
             if (t0 > 0) {
 #pragma unroll
-                for (int i = 0; i < kTokensPerPass; ++i)
-                    xv[i] = buffer_load<kStream>(xbuf, (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < KP; ++i)
+                        xv[r][i] = buffer_load<kStream>(
+                            xbuf[r], (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
             }
-            const int tokens = min(kTokensPerPass, p.t - t0);
-            u32x4 ov[kTokensPerPass];
+            const int tokens = min(KP, p.t - t0);
+            u32x4 ov[R][KP];
 #pragma unroll
-            for (int i = 0; i < kTokensPerPass; ++i) {
-                ov[i] = u32x4{0u, 0u, 0u, 0u};
-                if (i < tokens) {
-                    float y[kChPerLane];
+            for (int r = 0; r < R; ++r) {
+                const bool live = slot[r] >= 0;
 #pragma unroll
-                    for (int ch = 0; ch < kChPerLane; ++ch) {
-                        const int q = ch >> 1, hh = ch & 1;
-                        // history[L+1-W+j] for W = 4: positions L-3..L-1, then x;
-                        // exact BF16 products, j ascending, bias last.
-                        float acc = half_f32(pl[L - 3][q], hh) * wf[4 * ch + 0];
-                        acc = __builtin_fmaf(half_f32(pl[L - 2][q], hh), wf[4 * ch + 1], acc);
-                        acc = __builtin_fmaf(half_f32(pl[L - 1][q], hh), wf[4 * ch + 2], acc);
-                        acc = __builtin_fmaf(half_f32(xv[i][q], hh), wf[4 * ch + 3], acc);
-                        if (HAS_BIAS) acc += bf[ch];
-                        y[ch] = activate<ACT>(acc);
+                for (int i = 0; i < KP; ++i) {
+                    ov[r][i] = u32x4{0u, 0u, 0u, 0u};
+                    if (i < tokens) {
+                        // history[L+1-W+j] for W = 4: positions L-3..L-1, then x
+                        const u32x4 y = conv8<ACT>(pl[r][L - 3], pl[r][L - 2], pl[r][L - 1], xv[r][i], wf, bf);
+                        if (live) ov[r][i] = y;  // a padding row writes zeros
+                        // the shift: every position moves one place older, x is the newest
+#pragma unroll
+                        for (int k = 0; k < L - 1; ++k) pl[r][k] = pl[r][k + 1];
+                        pl[r][L - 1] = xv[r][i];
                     }
-                    if (live)  // a padding row writes zeros
-                        ov[i] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                                      pack_bf16x2(y[6], y[7])};
-                    // the shift: every position moves one place older, x is the newest
-#pragma unroll
-                    for (int k = 0; k < L - 1; ++k) pl[k] = pl[k + 1];
-                    pl[L - 1] = xv[i];
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kTokensPerPass; ++i)
-                buffer_store<kStream>(ov[i], obuf, (t0 + i < p.t ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < KP; ++i)
+                    buffer_store<kStream>(ov[r][i], obuf[r],
+                                          (t0 + i < p.t ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
         }
 
         // Write the final history back.
-        if (CHANNEL_LAST) {
 #pragma unroll
-            for (int k = 0; k < L; ++k) buffer_store<kStream>(pl[k], sbuf, plane_bytes * (uint32_t)k + lane_off);
-        } else {
-            u32x4 *stage = stage_all[wave];
-            uint32_t h[4 * L];
-            from_planes<L>(pl, h);
-            wave_lds_sync();
+        for (int r = 0; r < R; ++r) {
+            if (CHANNEL_LAST) {
 #pragma unroll
-            for (int k = 0; k < L; ++k) stage[lane * L + k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
-            wave_lds_sync();
-            u32x4 nv[L];
+                for (int k = 0; k < L; ++k) buffer_store<kStream>(pl[r][k], sbuf[r], plane_bytes * (uint32_t)k + lane_off);
+            } else {
+                u32x4 *stage = stage_all[wave];
+                uint32_t h[4 * L];
+                from_planes<L>(pl[r], h);
+                wave_lds_sync();
 #pragma unroll
-            for (int j = 0; j < L; ++j) nv[j] = stage[j * kWave + lane];
+                for (int k = 0; k < L; ++k) stage[lane * L + k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+                wave_lds_sync();
+                u32x4 nv[L];
 #pragma unroll
-            for (int j = 0; j < L; ++j) buffer_store<kStream>(nv[j], sbuf, (uint32_t)(j * kWave) * 16u + lane_bytes);
+                for (int j = 0; j < L; ++j) nv[j] = stage[j * kWave + lane];
+#pragma unroll
+                for (int j = 0; j < L; ++j)
+                    buffer_store<kStream>(nv[j], sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+            }
         }
         __syncthreads();  // the stage and the weight tile are reused by the next unit
     }
@@ -223,20 +239,35 @@ hipError_t launch_tokens(Kernel kernel, const TokensParams &p, int tiles_per_row
                            stream);
 }
 
-template <int L, int ACT, bool CL>
+template <int L, int ACT, bool CL, int R, int KP>
 hipError_t launch_tokens_l(const TokensParams &p, int tiles, hipStream_t stream) {
-    const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
-    return p.bias != nullptr ? launch_tokens(tokens_v8<L, ACT, true, CL>, p, tiles, block_units, kBlock, stream)
-                             : launch_tokens(tokens_v8<L, ACT, false, CL>, p, tiles, block_units, kBlock, stream);
+    const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock * R - 1) / (kWavesPerBlock * R));
+    return p.bias != nullptr ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP>, p, tiles, block_units, kBlock, stream)
+                             : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP>, p, tiles, block_units, kBlock, stream);
 }
 
 template <int ACT, bool CL>
 hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream, const char **name) {
-#define DCCONV_TOK_CASE(LL)                                                                                          \
-    case LL:                                                                                                         \
-        *name = CL ? (ACT ? "tokens_v8<L=" #LL ",silu,channel_last>" : "tokens_v8<L=" #LL ",identity,channel_last>") \
-                   : (ACT ? "tokens_v8<L=" #LL ",silu,compact>" : "tokens_v8<L=" #LL ",identity,compact>");          \
-        return launch_tokens_l<LL, ACT, CL>(p, tiles, stream);
+    // Two rows per wave (4 tokens per pass, to bound registers) when the
+    // history is short and the grid still fills the chip with them; else one
+    // row and 8 tokens per pass.
+    const bool two = p.l <= 4 && ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
+#define DCCONV_TOK_NAME(LL, RR)                                                              \
+    (CL ? (ACT ? "tokens_v8<L=" #LL ",silu,channel_last,R=" #RR ">"                         \
+               : "tokens_v8<L=" #LL ",identity,channel_last,R=" #RR ">")                    \
+        : (ACT ? "tokens_v8<L=" #LL ",silu,compact,R=" #RR ">" : "tokens_v8<L=" #LL ",identity,compact,R=" #RR ">"))
+#define DCCONV_TOK_CASE(LL)                                       \
+    case LL:                                                      \
+        *name = DCCONV_TOK_NAME(LL, 1);                           \
+        return launch_tokens_l<LL, ACT, CL, 1, 8>(p, tiles, stream);
+    if (two) {
+        if (p.l == 3) {
+            *name = DCCONV_TOK_NAME(3, 2);
+            return launch_tokens_l<3, ACT, CL, 2, 4>(p, tiles, stream);
+        }
+        *name = DCCONV_TOK_NAME(4, 2);
+        return launch_tokens_l<4, ACT, CL, 2, 4>(p, tiles, stream);
+    }
     switch (p.l) {
         DCCONV_TOK_CASE(3)
         DCCONV_TOK_CASE(4)
@@ -247,6 +278,7 @@ hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream
         default: return hipErrorInvalidValue;
     }
 #undef DCCONV_TOK_CASE
+#undef DCCONV_TOK_NAME
 }
 
 }  // namespace

@@ -127,14 +127,14 @@ def test_tokens_compact(L, T):
     case = TokensCase(1000 + 10 * L + T, N=6, D=1096, T=T, L=L, bias=T % 2 == 1,
                       act="silu" if T % 3 else None)
     case.check()
-    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("compact>"), case.kernel
+    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("compact,R=1>"), case.kernel
 
 
 @pytest.mark.parametrize("L", [5, 6, 7])
 def test_tokens_compact_other_history_lengths(L):
     case = TokensCase(1100 + L, N=5, D=520, T=11, L=L, bias=True, act="silu", routing="unique", S=9)
     case.check()
-    assert case.kernel == f"tokens_v8<L={L},silu,compact>", case.kernel
+    assert case.kernel == f"tokens_v8<L={L},silu,compact,R=1>", case.kernel
 
 
 @pytest.mark.parametrize("L", [3, 4, 5, 6, 7, 8])
@@ -143,7 +143,7 @@ def test_tokens_channel_last(L, T):
     case = TokensCase(1200 + 10 * L + T, N=7, D=1608, T=T, L=L, layout="channel_last", bias=L % 2 == 0,
                       act="silu" if T != 4 else None, routing="unique", S=11)
     case.check()
-    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("channel_last>"), case.kernel
+    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("channel_last,R=1>"), case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
@@ -166,7 +166,7 @@ def test_tokens_long_history_in_one_call():
     case.indices = case.oracle_indices = data["indices"]
     case.act, case.layout, case.out_layout, case.status = spec.act, spec.layout, "token_major", True
     assert case.check() == 0
-    assert case.kernel == "tokens_v8<L=8,identity,compact>", case.kernel
+    assert case.kernel == "tokens_v8<L=8,identity,compact,R=1>", case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
@@ -175,7 +175,18 @@ def test_tokens_full_size_large_decode(layout):
     checked element by element against the oracle at full size."""
     case = TokensCase(1400, N=256, D=8192, T=4, L=3, layout=layout, ldx=8200)
     case.check()
-    assert case.kernel == f"tokens_v8<L=3,silu,{layout}>", case.kernel
+    assert case.kernel == f"tokens_v8<L=3,silu,{layout},R=2>", case.kernel
+
+
+@pytest.mark.parametrize("layout", ["compact", "channel_last"])
+@pytest.mark.parametrize("T", [3, 7, 9])
+def test_tokens_two_rows_per_wave(layout, T):
+    """Enough rows for two per wave: odd N (a lone last row), padding rows,
+    bias, L = 4, token counts that leave a partial pass of 4."""
+    case = TokensCase(1450 + T, N=129, D=8192, T=T, L=4, layout=layout, bias=True, routing="padded", n_pad=9,
+                      S=160, status=True)
+    assert case.check() == 0
+    assert case.kernel == f"tokens_v8<L=4,silu,{layout},R=2>", case.kernel
 
 
 # ---------------------------------------------------------- routing and padding
