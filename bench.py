@@ -424,10 +424,12 @@ def main():
         for other in wl.CONFIGS + wl.EXTRA + wl.PREFILL:
             if other.name == spec.name:
                 continue
-            if isinstance(other, wl.PrefillSpec):  # ~60 us calls: fewer steps, sets beyond the 256 MB cache
-                r, _ = measure(other, max(20, args.steps // 20), 5, max(args.rotate_mb, 1024.0), args.launch)
+            # as many steps as the main workload (a replay of a few hundred steps still
+            # carries a fixed start-up cost of about 0.25 ms), fewer for ~0.1 ms prefill calls
+            if isinstance(other, wl.PrefillSpec):
+                r, _ = measure(other, max(100, args.steps // 5), 5, args.rotate_mb, args.launch)
             else:
-                r, _ = measure(other, max(200, args.steps // 5), 20, min(args.rotate_mb, 512.0), args.launch)
+                r, _ = measure(other, args.steps, args.warmup, args.rotate_mb, args.launch)
             log(f"[bench] {other.name}: {r['us_per_call']:.3f} us/call, {r['gbs']:.1f} GB/s, "
                 f"{r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}")
             entry = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
