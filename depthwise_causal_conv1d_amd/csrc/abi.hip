@@ -54,6 +54,27 @@ bool overlaps(const Span &a, const Span &b) {
 
 constexpr int64_t kI32Max = 2147483647;
 
+// Bytes spanned by an [e0, e1, e2] BF16 array at element strides st (strides
+// >= 0): 2 * (sum (e_i - 1) * st_i + 1), or 0 for an empty array.  False when
+// the span overflows or exceeds 2^47 bytes, more than any device address space.
+bool span_bytes(const int64_t e[3], const int64_t st[3], int64_t *bytes) {
+    const int64_t kMaxElems = (int64_t)1 << 46;
+    int64_t last = 0;
+    for (int i = 0; i < 3; ++i)
+        if (e[i] <= 0) {
+            *bytes = 0;
+            return true;
+        }
+    for (int i = 0; i < 3; ++i) {
+        int64_t term;
+        if (__builtin_mul_overflow(e[i] - 1, st[i], &term) || term > kMaxElems) return false;
+        last += term;
+        if (last > kMaxElems) return false;
+    }
+    *bytes = 2 * (last + 1);
+    return true;
+}
+
 
 // Metadata shared by both entry points: shapes, state strides, the served subset.
 int check_state_and_shapes(int64_t n, int64_t d, int64_t s, int64_t l, int64_t st_s, int64_t st_d, int64_t st_l,
@@ -72,6 +93,13 @@ int check_state_and_shapes(int64_t n, int64_t d, int64_t s, int64_t l, int64_t s
     if (w != 4) return fail(DCCONV_EUNSUPPORTED, "only filter width w=4 is served, got w=%lld", (long long)w);
     if (n > kI32Max || d > kI32Max || s > kI32Max || l > 65536)
         return fail(DCCONV_EUNSUPPORTED, "sizes beyond n, d, s < 2^31 and l <= 65536 are not served");
+    {
+        const int64_t e[3] = {s, d, l}, st[3] = {st_s, st_d, st_l};
+        int64_t bytes;
+        if (!span_bytes(e, st, &bytes))
+            return fail(DCCONV_EINVAL, "conv_state strides (%lld, %lld, %lld) span more than 2^47 bytes",
+                        (long long)st_s, (long long)st_d, (long long)st_l);
+    }
     if (st_l == 1 && st_d == l && (st_s >= d * l || s <= 1)) {
         *layout = dcconv::StateLayout::Compact;
     } else if (st_d == 1 && st_l == d && (st_s >= l * d || s <= 1)) {
@@ -103,9 +131,11 @@ int check_pointers(const void *x, int64_t x_bytes, void *conv_state, int64_t s, 
     if ((conv_state_indices && !aligned(conv_state_indices, 4)) || (dev_status && !aligned(dev_status, 4)))
         return fail(DCCONV_EINVAL, "conv_state_indices and dev_status must be 4-byte aligned");
     // nothing the call writes may alias anything else it touches
-    const int64_t state_elems = s > 0 ? (s - 1) * st_s + (d - 1) * st_d + (l - 1) * st_l + 1 : 0;
+    const int64_t se[3] = {s, d, l}, sst_[3] = {st_s, st_d, st_l};
+    int64_t state_bytes = 0;
+    span_bytes(se, sst_, &state_bytes);  // bounded by check_state_and_shapes
     const Span sx = span("x", x, x_bytes);
-    const Span sst = span("conv_state", conv_state, 2 * state_elems);
+    const Span sst = span("conv_state", conv_state, state_bytes);
     const Span sw = span("weight", weight, 2 * d * w);
     const Span sb = span("bias", bias, 2 * d);
     const Span si = span("conv_state_indices", conv_state_indices, 4 * n);
@@ -185,7 +215,11 @@ extern "C" int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
     if (cache_seqlens != nullptr && !aligned(cache_seqlens, 4))
         return fail(DCCONV_EINVAL, "cache_seqlens must be 4-byte aligned");
     const Span extra[] = {span("cache_seqlens", cache_seqlens, 4 * n)};
-    rc = check_pointers(x, 2 * ((n - 1) * ld_x + d), conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias,
+    const int64_t xe[3] = {n, d, 1}, xst[3] = {ld_x, 1, 0};
+    int64_t x_bytes;
+    if (!span_bytes(xe, xst, &x_bytes))
+        return fail(DCCONV_EINVAL, "x with row stride %lld spans more than 2^47 bytes", (long long)ld_x);
+    rc = check_pointers(x, x_bytes, conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias,
                         conv_state_indices, n, out, 2 * n * d, dev_status, extra, 1);
     if (rc != DCCONV_OK) return rc;
 
@@ -241,8 +275,10 @@ extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t
     if (!strides_distinct(ext, ost))
         return fail(DCCONV_EINVAL, "out strides (%lld, %lld, %lld) give two elements the same address",
                     (long long)os_n, (long long)os_d, (long long)os_t);
-    const int64_t x_bytes = 2 * ((n - 1) * xs_n + (d - 1) * xs_d + (t - 1) * xs_t + 1);
-    const int64_t out_bytes = 2 * ((n - 1) * os_n + (d - 1) * os_d + (t - 1) * os_t + 1);
+    const int64_t xst[3] = {xs_n, xs_d, xs_t};
+    int64_t x_bytes, out_bytes;
+    if (!span_bytes(ext, xst, &x_bytes) || !span_bytes(ext, ost, &out_bytes))
+        return fail(DCCONV_EINVAL, "x or out strides span more than 2^47 bytes");
     rc = check_pointers(x, x_bytes, conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias, conv_state_indices, n,
                         out, out_bytes, dev_status);
     if (rc != DCCONV_OK) return rc;
@@ -318,8 +354,9 @@ extern "C" int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
         if (!strides_distinct(ext, ost))
             return fail(DCCONV_EINVAL, "out strides (%lld, %lld, %lld) give two elements the same address",
                         (long long)os_n, (long long)os_d, (long long)os_t);
-        x_bytes = 2 * ((rows - 1) * xs_n + (d - 1) * xs_d + (t - 1) * xs_t + 1);
-        out_bytes = 2 * ((rows - 1) * os_n + (d - 1) * os_d + (t - 1) * os_t + 1);
+        const int64_t xst[3] = {xs_n, xs_d, xs_t};
+        if (!span_bytes(ext, xst, &x_bytes) || !span_bytes(ext, ost, &out_bytes))
+            return fail(DCCONV_EINVAL, "x or out strides span more than 2^47 bytes");
     }
     const Span extra[] = {span("seq_starts", seq_starts, 4 * (n + 1)), span("has_initial_state", has_initial_state, n)};
     rc = check_pointers(x, x_bytes, conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias, conv_state_indices, n,

@@ -94,6 +94,9 @@ DECLINES = [
     (dict(activation=2), dc.DCCONV_EINVAL, "activation"),
     (dict(st_d=-3), dc.DCCONV_EINVAL, "non-negative"),
     (dict(cache_seqlens=IX + 2), dc.DCCONV_EINVAL, "cache_seqlens must be 4-byte aligned"),
+    (dict(ld_x=1 << 50), dc.DCCONV_EINVAL, "2^47 bytes"),
+    (dict(st_s=1 << 50), dc.DCCONV_EINVAL, "2^47 bytes"),
+    (dict(st_s=(1 << 62) + 8), dc.DCCONV_EINVAL, "2^47 bytes"),
     (dict(cache_seqlens=OUT + 64), dc.DCCONV_EINVAL, "overlaps cache_seqlens"),
     (dict(w=3), dc.DCCONV_EUNSUPPORTED, "w=4"),
     (dict(w=5, l=4, st_d=4, st_s=256), dc.DCCONV_EUNSUPPORTED, "w=4"),
@@ -222,6 +225,8 @@ TOKEN_DECLINES = [
     (dict(t=-1), dc.DCCONV_EINVAL, "t (tokens)"),
     (dict(xs_t=-64), dc.DCCONV_EINVAL, "non-negative"),
     (dict(os_d=-1), dc.DCCONV_EINVAL, "non-negative"),
+    (dict(xs_t=1 << 61), dc.DCCONV_EINVAL, "2^47 bytes"),
+    (dict(os_n=1 << 48), dc.DCCONV_EINVAL, "2^47 bytes"),
     (dict(os_t=32), dc.DCCONV_EINVAL, "same address"),       # tokens overlap channels
     (dict(os_n=64), dc.DCCONV_EINVAL, "same address"),       # rows overlap tokens
     (dict(os_d=0), dc.DCCONV_EINVAL, "same address"),
@@ -274,6 +279,8 @@ def _pargs(**over):
 PREFILL_DECLINES = [
     (dict(t=-1), dc.DCCONV_EINVAL, "t (tokens)"),
     (dict(xs_t=-64), dc.DCCONV_EINVAL, "non-negative"),
+    (dict(xs_t=1 << 60), dc.DCCONV_EINVAL, "2^47 bytes"),
+    (dict(os_t=1 << 48), dc.DCCONV_EINVAL, "2^47 bytes"),
     (dict(conv_state=None), dc.DCCONV_EINVAL, "without conv_state"),                 # s = 4 without a state
     (dict(conv_state=None, s=0, conv_state_indices=IX), dc.DCCONV_EINVAL, "without conv_state"),
     (dict(conv_state=None, s=0, has_initial_state=HI), dc.DCCONV_EINVAL, "without conv_state"),

@@ -312,3 +312,36 @@ def test_prefill_packed_long_chunks_cross_many_sequences():
     lens = [int(v) for v in rng.integers(0, 40, size=3000)]
     case = PrefillCase(2900, 64, lens=lens, L=4, state="compact", routing="unique", S=3000, has_init="mixed")
     case.check()
+
+
+def test_prefill_in_hip_graph_chunked_continuation():
+    """A captured prefill that continues every sequence from its slot, replayed
+    with fresh tokens: each replay is the next chunk of the same sequences, and
+    matches the oracle continuing the same way."""
+    rng = np.random.default_rng(3000)
+    N, D, T, L = 4, 1024, 37, 3
+    st_h = _bf(rng, (N, L, D)); w_h = _bf(rng, (D, 4))
+    sd, wd = to_dev(st_h), to_dev(w_h)
+    sv = sd.permute(0, 2, 1)
+    xbuf = torch.empty(N, T, D, dtype=torch.bfloat16, device="cuda")
+    obuf = torch.empty(N, T, D, dtype=torch.bfloat16, device="cuda")
+    hi = torch.ones(N, dtype=torch.bool, device="cuda")
+    xbuf.copy_(to_dev(_bf(rng, (N, T, D))))
+    dc.causal_conv1d(xbuf.permute(0, 2, 1), wd, None, "silu", conv_state=sv, has_initial_state=hi,
+                     out=obuf.permute(0, 2, 1))  # warm
+    torch.cuda.synchronize()
+    ref_state = np.ascontiguousarray(from_dev(sd).transpose(0, 2, 1))   # oracle keeps it compact
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dc.causal_conv1d(xbuf.permute(0, 2, 1), wd, None, "silu", conv_state=sv, has_initial_state=hi,
+                         out=obuf.permute(0, 2, 1))
+    for step in range(4):
+        x_h = _bf(rng, (N, T, D))
+        xbuf.copy_(to_dev(x_h))
+        g.replay()
+        torch.cuda.synchronize()
+        ref, ref32 = oracle.prefill(x_h, N, D, T, (T * D, 1, D), w_h, None, "silu", state_buf=ref_state, S=N, L=L,
+                                    state_strides=(D * L, L, 1), has_init=np.ones(N, np.uint8), want_f32=True)
+        assert_outputs_match(from_dev(obuf), ref, ref32, what=f"replay {step}")
+        np.testing.assert_array_equal(from_dev(sd).transpose(0, 2, 1), ref_state)
+        _ = (xbuf.float() * 2).sum().item()  # eager work between replays

@@ -276,3 +276,32 @@ def test_tokens_zero_tokens_leave_everything():
     torch.cuda.synchronize()
     assert out.shape == (4, 64, 0)
     np.testing.assert_array_equal(from_dev(sd), st)
+
+
+def test_tokens_in_hip_graph_replays():
+    """A captured multi-token call, replayed with fresh tokens each time (copied
+    in eagerly between replays), matches the oracle stepping the same way."""
+    rng = np.random.default_rng(2200)
+    N, D, T, L = 64, 2048, 5, 4
+    st_h = _bf(rng, (N, D, L)); w_h = _bf(rng, (D, 4)); b_h = _bf(rng, (D,), 0.1)
+    sd, wd, bd = to_dev(st_h), to_dev(w_h), to_dev(b_h)
+    xbuf = torch.empty(N, T, D, dtype=torch.bfloat16, device="cuda")
+    obuf = torch.empty(N, T, D, dtype=torch.bfloat16, device="cuda")
+    x_view, o_view = xbuf.permute(0, 2, 1), obuf.permute(0, 2, 1)
+    xbuf.copy_(to_dev(_bf(rng, (N, T, D))))
+    dc.causal_conv1d_update_tokens(x_view, sd, wd, bd, "silu", out=o_view)  # warm
+    torch.cuda.synchronize()
+    ref_state = from_dev(sd)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dc.causal_conv1d_update_tokens(x_view, sd, wd, bd, "silu", out=o_view)
+    for step in range(4):
+        x_h = _bf(rng, (N, T, D))
+        xbuf.copy_(to_dev(x_h))
+        g.replay()
+        torch.cuda.synchronize()
+        ref, ref32 = oracle.update_tokens(x_h, N, D, T, (T * D, 1, D), ref_state, N, L, (D * L, L, 1), w_h, b_h,
+                                          None, "silu", want_f32=True)
+        assert_outputs_match(from_dev(obuf), ref, ref32, what=f"replay {step}")
+        np.testing.assert_array_equal(from_dev(sd), ref_state)
+        _ = (xbuf.float() * 2).sum().item()  # eager work between replays
