@@ -324,6 +324,29 @@ def config_of(spec, res, launch):
     return cfg
 
 
+def gpu_clocks():
+    """Current shader and memory clock (MHz) of the GPU in use, read from the
+    driver's DPM tables in sysfs (the level marked '*'); {} when unreadable."""
+    import torch
+    try:
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        bdf = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+    except Exception:
+        return {}
+    clocks = {}
+    for key, name in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+        try:
+            with open(f"/sys/bus/pci/devices/{bdf}/{name}") as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        clocks[key] = int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+        except (OSError, ValueError, IndexError):
+            pass
+    if clocks:
+        clocks["pci"] = bdf
+    return clocks
+
+
 def environment():
     import torch
     env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
@@ -333,6 +356,7 @@ def environment():
         env["cus"] = props.multi_processor_count
     except Exception:
         pass
+    env["clocks_after_run"] = gpu_clocks()
     try:
         cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")]
         env["host_cpu"] = cpu[0] if cpu else ""
@@ -442,6 +466,10 @@ def main():
         cpu = cpu_baseline(spec, host, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
 
+    # the same calls on one buffer set, resident in the 256 MB Infinity Cache: a
+    # cache figure, reported beside the HBM one and never as a fraction of HBM peak
+    warm, _ = measure(spec, args.steps, args.warmup, 0.0, args.launch)
+    log(f"[bench] {spec.name} warm (one buffer set, Infinity Cache resident): {warm['us_per_call']:.3f} us/call")
     floor_us = launch_floor()
     log(f"[bench] launch floor (empty fill kernel, graph replay): {floor_us:.3f} us/call; "
         f"{spec.name} in-kernel share: {res['bytes_per_call'] / ((res['us_per_call'] - floor_us) * 1e3):.1f} GB/s")
@@ -469,6 +497,8 @@ def main():
         # per-call floor of a graph-replayed launch, measured beside the workload: a call of
         # B bytes cannot exceed B / (B / peak + floor), the ceiling the fraction is read against
         "launch_floor_us": round(floor_us, 3),
+        "warm_cache": {"us_per_call": round(warm["us_per_call"], 4), "gbs": round(warm["gbs"], 1),
+                       "buffer_sets": warm["buffer_sets"], "note": "Infinity Cache resident, not an HBM figure"},
         "frac_ceiling_at_floor": round(res["bytes_per_call"] / (res["bytes_per_call"] / (PEAK_HBM_GBS * 1e3)
                                                                 + floor_us) / (PEAK_HBM_GBS * 1e3), 4),
         "cpu_baseline": cpu,

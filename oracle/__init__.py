@@ -37,13 +37,24 @@ class OracleError(ValueError):
         self.code = code
 
 
+_DRIVER = os.path.join(_HERE, "sanitize_driver.c")
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with the host C compiler (plain C99, no fast-math)."""
+    """Compile the oracle with the host C compiler (plain C99, no fast-math).
+    With ``force`` also compile the sanitizer driver (plain build here; the CPU
+    test suite builds it again with AddressSanitizer and UBSan), so every C
+    source of the oracle is known to compile."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
         subprocess.run(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
                         "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
+    if force:
+        out_dir = os.path.join(_HERE, "_build")
+        os.makedirs(out_dir, exist_ok=True)
+        subprocess.run(["gcc", "-std=c99", "-O1", "-ffp-contract=off", "-o", os.path.join(out_dir, "sanitize_driver"),
+                        _SRC, _DRIVER, "-lm"], check=True)
     return _LIB
 
 
