@@ -245,18 +245,21 @@ def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None, *,
 
 
 def causal_conv1d_update_tokens(x, conv_state, weight, bias=None, activation=None, *, conv_state_indices=None,
-                                out=None, dev_status=None):
+                                cache_seqlens=None, out=None, dev_status=None):
     """T successive decode steps in one call: x is [N, D, T] (any strides), the
     multi-token form the page reserves.  ``conv_state`` is updated in place (each
     selected slot read and written once); returns out [N, D, T], by default
-    stored token-major (a view of a contiguous [N, T, D] buffer)."""
+    stored token-major (a view of a contiguous [N, T, D] buffer).  With
+    ``cache_seqlens`` the state is a circular buffer, token t of row n being the
+    (cache_seqlens[n] + t)-th token its slot sees."""
     import torch
 
     if x.dim() != 3:
         raise ValueError(f"x must be [N, D, T], got shape {tuple(x.shape)}")
     N, D, T = x.shape
     x2 = x[:, :, 0] if T > 0 else x.new_empty(N, D)
-    _check_tensors(x2, conv_state, weight, bias, conv_state_indices, None, activation, x_unit_channel_stride=False)
+    _check_tensors(x2, conv_state, weight, bias, conv_state_indices, cache_seqlens, activation,
+                   x_unit_channel_stride=False)
     if x.dtype != torch.bfloat16:
         raise ValueError(f"x must be bfloat16, got {x.dtype}")
     if out is None:
@@ -271,7 +274,8 @@ def causal_conv1d_update_tokens(x, conv_state, weight, bias=None, activation=Non
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
         rc = dcconv_update_tokens(_ptr(x), N, D, T, xs[0], xs[1], xs[2], _ptr(conv_state), S, L, st[0], st[1], st[2],
-                                  _ptr(weight), weight.shape[1], _ptr(bias), _ptr(conv_state_indices), None,
+                                  _ptr(weight), weight.shape[1], _ptr(bias), _ptr(conv_state_indices),
+                                  _ptr(cache_seqlens),
                                   _ACTIVATIONS[activation], _ptr(out), os_[0], os_[1], os_[2], _ptr(dev_status),
                                   stream)
     _raise_for(rc)

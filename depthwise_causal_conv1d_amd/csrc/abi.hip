@@ -265,10 +265,6 @@ extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t
         return fail(DCCONV_EINVAL, "x and out strides must be non-negative");
     int rc = check_state_and_shapes(n, d, s, l, st_s, st_d, st_l, w, activation, &layout);
     if (rc != DCCONV_OK) return rc;
-    if (cache_seqlens != nullptr)
-        return fail(DCCONV_EUNSUPPORTED,
-                    "cache_seqlens (circular-buffer state) is served by dcconv_update only, not by the "
-                    "multi-token update");
     if (t > kI32Max) return fail(DCCONV_EUNSUPPORTED, "t >= 2^31 tokens is not served");
     if (n == 0 || t == 0) return succeed("");
     const int64_t ext[3] = {n, d, t}, ost[3] = {os_n, os_d, os_t};
@@ -279,8 +275,11 @@ extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t
     int64_t x_bytes, out_bytes;
     if (!span_bytes(ext, xst, &x_bytes) || !span_bytes(ext, ost, &out_bytes))
         return fail(DCCONV_EINVAL, "x or out strides span more than 2^47 bytes");
+    if (cache_seqlens != nullptr && !aligned(cache_seqlens, 4))
+        return fail(DCCONV_EINVAL, "cache_seqlens must be 4-byte aligned");
+    const Span extra[] = {span("cache_seqlens", cache_seqlens, 4 * n)};
     rc = check_pointers(x, x_bytes, conv_state, s, d, l, st_s, st_d, st_l, weight, w, bias, conv_state_indices, n,
-                        out, out_bytes, dev_status);
+                        out, out_bytes, dev_status, extra, 1);
     if (rc != DCCONV_OK) return rc;
 
     dcconv::TokensParams p;
@@ -289,6 +288,7 @@ extern "C" int dcconv_update_tokens(const void *x, int64_t n, int64_t d, int64_t
     p.weight = static_cast<const uint16_t *>(weight);
     p.bias = static_cast<const uint16_t *>(bias);
     p.idx = conv_state_indices;
+    p.seqlens = cache_seqlens;
     p.status = dev_status;
     p.out = static_cast<uint16_t *>(out);
     p.xs_n = xs_n;

@@ -32,6 +32,7 @@ struct TokensParams {
     const uint16_t *weight;
     const uint16_t *bias;
     const int32_t *idx;
+    const int32_t *seqlens;  // int32 [n] (circular-buffer state) or nullptr
     int32_t *status;
     uint16_t *out;
     int64_t xs_n, xs_d, xs_t;
@@ -69,6 +70,10 @@ hipError_t launch_update_ring(const UpdateParams &p, StateLayout layout, int act
 
 hipError_t launch_update_tokens(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
                                 const char **kernel_name);
+
+// The circular-buffer form of launch_update_tokens (p.seqlens != nullptr).
+hipError_t launch_update_tokens_ring(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
+                                     const char **kernel_name);
 
 hipError_t launch_prefill(const PrefillParams &p, StateLayout layout, int activation, hipStream_t stream,
                           const char **kernel_name);

@@ -15,6 +15,8 @@
 //    computed and every store after the last (the structure of the shifting
 //    update's kernels).
 //  * update_ring_scalar<ACT>: one thread per (row, channel), any layout.
+//  * tokens_ring_v8<ACT, HAS_BIAS> / tokens_ring_scalar<ACT>: T tokens per call
+//    on the same ring (the multi-token entry with cache_seqlens).
 #include <stdint.h>
 
 #include "dcconv.h"
@@ -172,7 +174,189 @@ hipError_t launch_ring(Kernel kernel, const UpdateParams &p, int tiles, int64_t 
                            stream);
 }
 
+// ---- T tokens per call on a ring ----------------------------------------------
+// Token i of row n is the (c + i)-th token its slot sees: its taps are tokens
+// c+i-3 .. c+i-1 (the first three come from the ring, later ones from this
+// call's x) and it lands at position (c + i) mod L.  Only the last min(T, L)
+// tokens survive in the ring, so only they are written; a window of the three
+// previous tokens rides in registers, so no tap is read back after a write.
+
+constexpr uint32_t kBadToken = 1u << 30;  // beyond every descriptor here (all < 2^30 bytes)
+constexpr int kRingPass = 8;              // tokens per load pass
+
+// The row's slot (or -1) and its count, as route_ring_row for a TokensParams.
+__device__ __forceinline__ int route_ring_tokens_row(const TokensParams &p, int row, int lane, int *seen) {
+    const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
+    *seen = p.seqlens[row];
+    if (*seen < 0) {
+        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQLEN);
+        return -1;
+    }
+    return slot;
+}
+
+template <int ACT, bool HAS_BIAS>
+__global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int tiles, int64_t block_units) {
+    __shared__ u32x4 weight_tile[4 * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
+    const int L = p.l;
+
+    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+        const int tile = (int)(bu % tiles);
+        const int row_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
+        const int c0 = tile * kChPerWave;
+        const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
+        const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+        const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
+        int c = 0;
+        const int slot = __builtin_amdgcn_readfirstlane(row_raw < p.n ? route_ring_tokens_row(p, row_raw, lane, &c) : -2);
+        const int head = __builtin_amdgcn_readfirstlane(c) % L;  // ring position of token c; c >= 0 when live
+        const bool live = slot >= 0;
+        const int row = min(row_raw, p.n - 1);
+
+        __builtin_amdgcn_s_setprio(3);
+        u32x4 wraw[kWeightChunks];
+        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        const Buffer sbuf = make_buffer(p.state + (int64_t)(live ? slot : 0) * p.st_s + c0,
+                                        live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+        u32x4 h[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int pos = head - 3 + k < 0 ? head - 3 + k + L : head - 3 + k;  // token c-3+k
+            h[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)pos + lane_off);
+        }
+        const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+        const Buffer obuf = make_buffer(p.out + (int64_t)row * p.os_n + c0,
+                                        row_raw < p.n ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+        u32x4 xv[kRingPass];
+#pragma unroll
+        for (int i = 0; i < kRingPass; ++i)
+            xv[i] = buffer_load<kStream>(xbuf, (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
+        __builtin_amdgcn_s_setprio(0);
+
+        float wf[32], bf[8];
+        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        unpack_bias(bv, bf);
+        const int keep_from = p.t - min(p.t, L);  // tokens from here on stay in the ring
+
+        for (int t0 = 0; t0 < p.t; t0 += kRingPass) {
+            if (t0 > 0) {
+#pragma unroll
+                for (int i = 0; i < kRingPass; ++i)
+                    xv[i] = buffer_load<kStream>(xbuf, (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+            }
+            u32x4 ov[kRingPass];
+#pragma unroll
+            for (int i = 0; i < kRingPass; ++i) {
+                const u32x4 y = conv8<ACT>(h[0], h[1], h[2], xv[i], wf, bf);
+                ov[i] = live ? y : u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
+                h[0] = h[1];
+                h[1] = h[2];
+                h[2] = xv[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kRingPass; ++i) {
+                const int tok = t0 + i;
+                buffer_store<kStream>(ov[i], obuf, (tok < p.t ? o_tok * (uint32_t)tok : kBadToken) + lane_off);
+                // a surviving token goes to ring position (c + tok) mod L
+                int pos = head + tok % L;
+                pos = pos >= L ? pos - L : pos;
+                buffer_store<kStream>(xv[i], sbuf,
+                                      (tok >= keep_from && tok < p.t ? plane_bytes * (uint32_t)pos : kBadToken) + lane_off);
+            }
+        }
+        __syncthreads();  // the weight tile is reused by the next unit
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kScalarBlock) void tokens_ring_scalar(TokensParams p, int tiles_per_row, int64_t units) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int row = (int)(unit / tiles_per_row);
+        const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
+        int seen = 0;
+        const int slot = route_ring_tokens_row(p, row, lane, &seen);
+        if (c >= p.d) continue;
+        uint16_t *o = p.out + (int64_t)row * p.os_n + (int64_t)c * p.os_d;
+        if (slot < 0) {
+            for (int t = 0; t < p.t; ++t) o[(int64_t)t * p.os_t] = 0;
+            continue;
+        }
+        const int L = p.l;
+        uint16_t *ring = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
+        const int64_t sl = p.st_l;
+        const uint16_t *xc = p.x + (int64_t)row * p.xs_n + (int64_t)c * p.xs_d;
+        const uint16_t *wt = p.weight + (int64_t)c * 4;
+        const float w0 = bf16_bits_to_f32(wt[0]), w1 = bf16_bits_to_f32(wt[1]);
+        const float w2 = bf16_bits_to_f32(wt[2]), w3 = bf16_bits_to_f32(wt[3]);
+        const float b = p.bias != nullptr ? bf16_bits_to_f32(p.bias[c]) : 0.0f;
+        float h0 = bf16_bits_to_f32(ring[(int64_t)ring_pos(seen - 3, L) * sl]);
+        float h1 = bf16_bits_to_f32(ring[(int64_t)ring_pos(seen - 2, L) * sl]);
+        float h2 = bf16_bits_to_f32(ring[(int64_t)ring_pos(seen - 1, L) * sl]);
+        for (int t = 0; t < p.t; ++t) {
+            const uint16_t xb = xc[(int64_t)t * p.xs_t];
+            const float xv = bf16_bits_to_f32(xb);
+            float acc = h0 * w0;
+            acc = __builtin_fmaf(h1, w1, acc);
+            acc = __builtin_fmaf(h2, w2, acc);
+            acc = __builtin_fmaf(xv, w3, acc);
+            acc += b;
+            o[(int64_t)t * p.os_t] = f32_to_bf16_bits(activate<ACT>(acc));
+            ring[(int64_t)ring_pos(seen + t, L) * sl] = xb;  // in order: a later token overwrites an earlier one
+            h0 = h1;
+            h1 = h2;
+            h2 = xv;
+        }
+    }
+}
+
+template <typename Kernel>
+hipError_t launch_tokens_ring(Kernel kernel, const TokensParams &p, int tiles, int64_t units, int block,
+                              hipStream_t stream) {
+    const int64_t blocks = units < kMaxBlocks ? units : kMaxBlocks;
+    TokensParams args_p = p;
+    int tiles_arg = tiles;
+    int64_t units_arg = units;
+    void *args[] = {&args_p, &tiles_arg, &units_arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(block), args, 0,
+                           stream);
+}
+
 }  // namespace
+
+hipError_t launch_update_tokens_ring(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
+                                     const char **kernel_name) {
+    const bool silu = activation == DCCONV_ACT_SILU;
+    const int64_t lim = (int64_t)1 << 30;
+    const bool v8 = layout == StateLayout::ChannelLast && p.d % kChPerLane == 0 && p.xs_d == 1 && p.os_d == 1 &&
+                    (p.n == 1 || (p.xs_n % 8 == 0 && p.os_n % 8 == 0)) &&
+                    (p.t == 1 || (p.xs_t % 8 == 0 && p.os_t % 8 == 0)) && p.st_s % kChPerLane == 0 &&
+                    p.xs_t * 2 * (int64_t)(p.t - 1) + 2 * kChPerWave < lim &&
+                    p.os_t * 2 * (int64_t)(p.t - 1) + 2 * kChPerWave < lim &&
+                    (int64_t)p.l * p.st_l * 2 + 2 * kChPerWave < lim;
+    if (v8) {
+        const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
+        const int64_t units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+        *kernel_name = silu ? "tokens_ring_v8<silu>" : "tokens_ring_v8<identity>";
+        if (p.bias != nullptr)
+            return silu ? launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_SILU, true>, p, tiles, units, kBlock, stream)
+                        : launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_IDENTITY, true>, p, tiles, units, kBlock, stream);
+        return silu ? launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_SILU, false>, p, tiles, units, kBlock, stream)
+                    : launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_IDENTITY, false>, p, tiles, units, kBlock, stream);
+    }
+    const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
+    const int64_t units = (int64_t)p.n * tiles;
+    *kernel_name = silu ? "tokens_ring_scalar<silu>" : "tokens_ring_scalar<identity>";
+    return silu ? launch_tokens_ring(tokens_ring_scalar<DCCONV_ACT_SILU>, p, tiles, units, kScalarBlock, stream)
+                : launch_tokens_ring(tokens_ring_scalar<DCCONV_ACT_IDENTITY>, p, tiles, units, kScalarBlock, stream);
+}
 
 hipError_t launch_update_ring(const UpdateParams &p, StateLayout layout, int activation, hipStream_t stream,
                               const char **kernel_name) {

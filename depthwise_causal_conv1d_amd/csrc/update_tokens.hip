@@ -285,6 +285,7 @@ hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream
 
 hipError_t launch_update_tokens(const TokensParams &p, StateLayout layout, int activation, hipStream_t stream,
                                 const char **kernel_name) {
+    if (p.seqlens != nullptr) return launch_update_tokens_ring(p, layout, activation, stream, kernel_name);
     const bool silu = activation == DCCONV_ACT_SILU;
     const int64_t lim = (int64_t)1 << 30;
     // The vector path needs 16-byte channel vectors everywhere and every buffer

@@ -153,8 +153,11 @@ int dcconv_update(const void *x, int64_t n, int64_t d, int64_t ld_x,
  * n, d, t     rows, channels, tokens (t == 0 or n == 0: DCCONV_OK, nothing enqueued).
  * out         BF16, element (r, c, t) at out[r*os_n + c*os_d + t*os_t]; the strides
  *             must give every element its own address (no two (r, c, t) alias).
- * cache_seqlens must be NULL here (circular-buffer state is served by
- * dcconv_update only; DCCONV_EUNSUPPORTED otherwise).
+ * cache_seqlens  NULL, or int32 [n]: circular-buffer state as for
+ * dcconv_update; token t of row r is the (cache_seqlens[r] + t)-th token its
+ * slot sees: its taps are tokens c+t-3 .. c+t-1 (from the ring for the first
+ * three, from x after that) and it lands at position (c + t) mod l.  Only the
+ * last min(t, l) tokens remain in the ring; the count is only read.
  * conv_state, s, l, st_*, weight, w, bias, conv_state_indices,
  * activation, dev_status, stream: exactly as for dcconv_update (the routing of a
  * row is the same for all of its tokens; a padding or rejected row writes zeros

@@ -230,7 +230,8 @@ TOKEN_DECLINES = [
     (dict(os_t=32), dc.DCCONV_EINVAL, "same address"),       # tokens overlap channels
     (dict(os_n=64), dc.DCCONV_EINVAL, "same address"),       # rows overlap tokens
     (dict(os_d=0), dc.DCCONV_EINVAL, "same address"),
-    (dict(cache_seqlens=IX), dc.DCCONV_EUNSUPPORTED, "cache_seqlens"),
+    (dict(cache_seqlens=IX + 2), dc.DCCONV_EINVAL, "cache_seqlens must be 4-byte aligned"),
+    (dict(cache_seqlens=OUT + 64), dc.DCCONV_EINVAL, "overlaps cache_seqlens"),
     (dict(w=3), dc.DCCONV_EUNSUPPORTED, "w=4"),
     (dict(l=2, st_d=2, st_s=128), dc.DCCONV_EINVAL, "must be >= w-1"),
     (dict(x=X + 8), dc.DCCONV_EINVAL, "16-byte aligned"),

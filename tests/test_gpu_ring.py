@@ -201,3 +201,91 @@ def test_ring_in_hip_graph_with_advancing_counts():
         np.testing.assert_array_equal(from_dev(sd), ref_state.transpose(0, 2, 1))
         np.testing.assert_array_equal(cd.cpu().numpy(), c_h)
         _ = (xd.float() * 2).sum().item()  # eager work between replays
+
+
+# ----------------------------------------------------- T tokens per call on a ring
+
+
+def _ring_tokens_reference(x_ntd, state_compact, weight, bias, indices, seqlens, act):
+    """The oracle's ring step applied token by token (count advanced each token)."""
+    N, T, D = x_ntd.shape
+    S, _, L = state_compact.shape
+    outs, outs32 = [], []
+    c = seqlens.copy()
+    for t in range(T):
+        o, o32 = oracle.update_ring(np.ascontiguousarray(x_ntd[:, t]), N, D, D, state_compact, S, L, (D * L, L, 1),
+                                    weight, bias, indices, c, act, want_f32=True)
+        outs.append(o); outs32.append(o32)
+        c = c + 1
+    return np.stack(outs, 1), np.stack(outs32, 1)
+
+
+@pytest.mark.parametrize("layout", ["channel_last", "compact"])
+@pytest.mark.parametrize("L,T", [(3, 1), (3, 5), (3, 9), (4, 3), (4, 20), (8, 6), (8, 17)])
+def test_ring_tokens(layout, L, T):
+    rng = np.random.default_rng(3600 + 10 * L + T)
+    N, D, S = 9, 1096, 12
+    x = _bf(rng, (N, T, D)); w = _bf(rng, (D, 4)); b = _bf(rng, (D,), 0.1)
+    st = _bf(rng, (S, D, L))                                     # compact values
+    idx = rng.choice(S, N, replace=False).astype(np.int32)
+    idx[4] = -1
+    seen = rng.integers(0, 50, size=N).astype(np.int32)
+    seen[:3] = [0, 1, 2]
+    ref_state = st.copy()
+    oi = idx.copy()
+    ref, ref32 = _ring_tokens_reference(x, ref_state, w, b, oi, seen, "silu")
+    phys = st if layout == "compact" else np.ascontiguousarray(st.transpose(0, 2, 1))
+    sb, sd = guarded_copy(phys)
+    sv = sd if layout == "compact" else sd.permute(0, 2, 1)
+    ob, od = guarded_empty((N * T * D,))
+    out = torch.as_strided(od, (N, D, T), (T * D, 1, D))
+    dc.causal_conv1d_update_tokens(to_dev(x).permute(0, 2, 1), sv, to_dev(w), to_dev(b), "silu",
+                                   conv_state_indices=torch.from_numpy(idx).cuda(),
+                                   cache_seqlens=torch.from_numpy(seen).cuda(), out=out)
+    kernel = dc.dcconv_last_kernel()
+    torch.cuda.synchronize()
+    assert_guards_intact(sb)
+    assert_guards_intact(ob)
+    got_state = from_dev(sd)
+    if layout == "channel_last":
+        got_state = got_state.transpose(0, 2, 1)
+    np.testing.assert_array_equal(got_state, ref_state, err_msg="ring not bit-exact")
+    assert_outputs_match(from_dev(out.permute(0, 2, 1)), ref, ref32)
+    assert kernel == ("tokens_ring_v8<silu>" if layout == "channel_last" else "tokens_ring_scalar<silu>"), kernel
+
+
+def test_ring_tokens_equal_single_ring_steps_on_gpu():
+    """T tokens through the multi-token entry == T single ring steps with the
+    count advanced in between, bit for bit."""
+    rng = np.random.default_rng(3700)
+    N, D, L, T = 32, 4096, 3, 7
+    x = _bf(rng, (N, T, D)); w = to_dev(_bf(rng, (D, 4)))
+    st = _bf(rng, (N, L, D))
+    c = rng.integers(0, 100, size=N).astype(np.int32)
+    s1, s2 = to_dev(st), to_dev(st)
+    xd = to_dev(x)
+    o1 = dc.causal_conv1d_update_tokens(xd.permute(0, 2, 1), s1.permute(0, 2, 1), w, None, "silu",
+                                        cache_seqlens=torch.from_numpy(c).cuda())
+    cd = torch.from_numpy(c).cuda()
+    outs = []
+    for t in range(T):
+        outs.append(dc.causal_conv1d_update(xd[:, t].contiguous(), s2.permute(0, 2, 1), w, None, "silu",
+                                            cache_seqlens=cd))
+        cd += 1
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(from_dev(o1.permute(0, 2, 1)), np.stack([from_dev(o) for o in outs], 1))
+    np.testing.assert_array_equal(from_dev(s1), from_dev(s2))
+
+
+def test_ring_tokens_bad_count_rejects_row():
+    rng = np.random.default_rng(3800)
+    N, D, L, T = 4, 512, 4, 3
+    st = _bf(rng, (N, L, D)); sd = to_dev(st)
+    seen = torch.tensor([5, -1, 0, 2], dtype=torch.int32, device="cuda")
+    stat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = dc.causal_conv1d_update_tokens(to_dev(_bf(rng, (N, T, D))).permute(0, 2, 1), sd.permute(0, 2, 1),
+                                         to_dev(_bf(rng, (D, 4))), None, "silu", cache_seqlens=seen, dev_status=stat)
+    torch.cuda.synchronize()
+    assert int(stat.item()) == dc.DCCONV_DEV_BAD_SEQLEN
+    assert np.all(wl.bf16_bits_to_f32(from_dev(out.permute(0, 2, 1))[1]) == 0)
+    np.testing.assert_array_equal(from_dev(sd)[1], st[1])
