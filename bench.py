@@ -46,7 +46,8 @@ def log(*a):
 def kernel_source_hash(kernel: str) -> str:
     """Hash of the sources a kernel is compiled from (its file and the shared
     device helpers), so stale counter summaries are recognised."""
-    main = ("update_tokens.hip" if kernel.startswith("tokens_") else
+    main = ("update_ring.hip" if kernel.startswith("tokens_ring") else
+            "update_tokens.hip" if kernel.startswith("tokens_") else
             "prefill.hip" if kernel.startswith("prefill_") else
             "update_ring.hip" if kernel.startswith("update_ring") else "update.hip")
     h = hashlib.sha256()
@@ -125,7 +126,7 @@ class Workload:
             # x [T, N, ld] seen as [N, D, T]; out [N, T, D] seen as [N, D, T]
             dc.causal_conv1d_update_tokens(s["x"][:, :, :D].permute(1, 2, 0), s["state"], s["weight"], s["bias"],
                                            self.spec.act, out=s["out"].permute(0, 2, 1),
-                                           conv_state_indices=s["idx"])
+                                           conv_state_indices=s["idx"], cache_seqlens=self.seqlens)
             return
         t = (i // self.n_sets) % self.spec.T
         dc.causal_conv1d_update_out(s["x"][t, :, :D], s["state"], s["weight"], s["bias"],
@@ -254,8 +255,10 @@ def cpu_baseline(spec, host, seconds: float):
         st = host["state"].copy()
         t0 = time.perf_counter()
         if spec.ring:
-            oracle.update_ring(x, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
-                               host["weight"], host["bias"], host["indices"], host["seqlens"], spec.act)
+            for t in range(tokens):  # a multi-token ring call is its tokens' ring steps in order
+                xt = np.ascontiguousarray(host["x"][t])
+                oracle.update_ring(xt, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
+                                   host["weight"], host["bias"], host["indices"], host["seqlens"] + t, spec.act)
         elif tokens == 1:
             oracle.update_strided(x, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
                                   host["weight"], host["bias"], host["indices"], spec.act)

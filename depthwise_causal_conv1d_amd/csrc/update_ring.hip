@@ -182,7 +182,6 @@ hipError_t launch_ring(Kernel kernel, const UpdateParams &p, int tiles, int64_t 
 // previous tokens rides in registers, so no tap is read back after a write.
 
 constexpr uint32_t kBadToken = 1u << 30;  // beyond every descriptor here (all < 2^30 bytes)
-constexpr int kRingPass = 8;              // tokens per load pass
 
 // The row's slot (or -1) and its count, as route_ring_row for a TokensParams.
 __device__ __forceinline__ int route_ring_tokens_row(const TokensParams &p, int row, int lane, int *seen) {
@@ -195,81 +194,116 @@ __device__ __forceinline__ int route_ring_tokens_row(const TokensParams &p, int 
     return slot;
 }
 
-template <int ACT, bool HAS_BIAS>
+// R rows per wave, KP tokens per pass; L3: the ring holds exactly the three
+// taps, so its planes are loaded in plane order before the count arrives and
+// rotated by c mod 3 afterwards (as in update_ring_v8).
+template <int ACT, bool HAS_BIAS, int R, int KP, bool L3>
 __global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int tiles, int64_t block_units) {
     __shared__ u32x4 weight_tile[4 * kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
-    const int L = p.l;
+    const int L = L3 ? 3 : p.l;
 
     for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
         const int tile = (int)(bu % tiles);
-        const int row_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
+        const int group = (int)(bu / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
         const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
-        int c = 0;
-        const int slot = __builtin_amdgcn_readfirstlane(row_raw < p.n ? route_ring_tokens_row(p, row_raw, lane, &c) : -2);
-        const int head = __builtin_amdgcn_readfirstlane(c) % L;  // ring position of token c; c >= 0 when live
-        const bool live = slot >= 0;
-        const int row = min(row_raw, p.n - 1);
+        int slot[R], head[R];  // head: ring position of token c (c mod L; c >= 0 for a live row)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = group * R + r;
+            int c = 0;
+            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_ring_tokens_row(p, row, lane, &c) : -2);
+            head[r] = __builtin_amdgcn_readfirstlane(c) % L;
+        }
 
         __builtin_amdgcn_s_setprio(3);
         u32x4 wraw[kWeightChunks];
         weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
-        const Buffer sbuf = make_buffer(p.state + (int64_t)(live ? slot : 0) * p.st_s + c0,
-                                        live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
-        u32x4 h[3];
+        Buffer sbuf[R], xbuf[R], obuf[R];
+        u32x4 h[R][3], xv[R][KP];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int pos = head - 3 + k < 0 ? head - 3 + k + L : head - 3 + k;  // token c-3+k
-            h[k] = buffer_load<kStream>(sbuf, plane_bytes * (uint32_t)pos + lane_off);
+        for (int r = 0; r < R; ++r) {
+            const bool live = slot[r] >= 0;
+            const int row = min(group * R + r, p.n - 1);
+            sbuf[r] = make_buffer(p.state + (int64_t)(live ? slot[r] : 0) * p.st_s + c0,
+                                  live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                // L3: plane k, rotated below; else token c-3+k's position
+                const int pos = L3 ? k : (head[r] - 3 + k < 0 ? head[r] - 3 + k + L : head[r] - 3 + k);
+                h[r][k] = buffer_load<kStream>(sbuf[r], plane_bytes * (uint32_t)pos + lane_off);
+            }
+            xbuf[r] = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+            obuf[r] = make_buffer(p.out + (int64_t)row * p.os_n + c0,
+                                  slot[r] != -2 ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+#pragma unroll
+            for (int i = 0; i < KP; ++i)
+                xv[r][i] = buffer_load<kStream>(xbuf[r], (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
         }
-        const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
-        const Buffer obuf = make_buffer(p.out + (int64_t)row * p.os_n + c0,
-                                        row_raw < p.n ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
-        u32x4 xv[kRingPass];
-#pragma unroll
-        for (int i = 0; i < kRingPass; ++i)
-            xv[i] = buffer_load<kStream>(xbuf, (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
         __builtin_amdgcn_s_setprio(0);
+        if (L3) {
+            // tap k (token c-3+k) is plane (c + k) mod 3
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const u32x4 p0 = h[r][0], p1 = h[r][1], p2 = h[r][2];
+                h[r][0] = head[r] == 0 ? p0 : head[r] == 1 ? p1 : p2;
+                h[r][1] = head[r] == 0 ? p1 : head[r] == 1 ? p2 : p0;
+                h[r][2] = head[r] == 0 ? p2 : head[r] == 1 ? p0 : p1;
+            }
+        }
 
         float wf[32], bf[8];
         weight_tile_share(weight_tile, wraw, wave, lane, wf);
         unpack_bias(bv, bf);
         const int keep_from = p.t - min(p.t, L);  // tokens from here on stay in the ring
 
-        for (int t0 = 0; t0 < p.t; t0 += kRingPass) {
+        for (int t0 = 0; t0 < p.t; t0 += KP) {
             if (t0 > 0) {
 #pragma unroll
-                for (int i = 0; i < kRingPass; ++i)
-                    xv[i] = buffer_load<kStream>(xbuf, (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
-            }
-            u32x4 ov[kRingPass];
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int i = 0; i < kRingPass; ++i) {
-                const u32x4 y = conv8<ACT>(h[0], h[1], h[2], xv[i], wf, bf);
-                ov[i] = live ? y : u32x4{0u, 0u, 0u, 0u};  // a padding row writes zeros
-                h[0] = h[1];
-                h[1] = h[2];
-                h[2] = xv[i];
+                    for (int i = 0; i < KP; ++i)
+                        xv[r][i] = buffer_load<kStream>(
+                            xbuf[r], (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+            }
+            const int tokens = min(KP, p.t - t0);
+            u32x4 ov[R][KP];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int i = 0; i < KP; ++i) {
+                    ov[r][i] = u32x4{0u, 0u, 0u, 0u};
+                    if (i < tokens) {
+                        const u32x4 y = conv8<ACT>(h[r][0], h[r][1], h[r][2], xv[r][i], wf, bf);
+                        if (slot[r] >= 0) ov[r][i] = y;  // a padding row writes zeros
+                        h[r][0] = h[r][1];
+                        h[r][1] = h[r][2];
+                        h[r][2] = xv[r][i];
+                    }
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kRingPass; ++i) {
-                const int tok = t0 + i;
-                buffer_store<kStream>(ov[i], obuf, (tok < p.t ? o_tok * (uint32_t)tok : kBadToken) + lane_off);
-                // a surviving token goes to ring position (c + tok) mod L
-                int pos = head + tok % L;
-                pos = pos >= L ? pos - L : pos;
-                buffer_store<kStream>(xv[i], sbuf,
-                                      (tok >= keep_from && tok < p.t ? plane_bytes * (uint32_t)pos : kBadToken) + lane_off);
-            }
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < KP; ++i) {
+                    const int tok = t0 + i;
+                    buffer_store<kStream>(ov[r][i], obuf[r], (tok < p.t ? o_tok * (uint32_t)tok : kBadToken) + lane_off);
+                    // a surviving token goes to ring position (c + tok) mod L
+                    int pos = head[r] + tok % L;
+                    pos = pos >= L ? pos - L : pos;
+                    buffer_store<kStream>(xv[r][i], sbuf[r],
+                                          (tok >= keep_from && tok < p.t ? plane_bytes * (uint32_t)pos : kBadToken) +
+                                              lane_off);
+                }
         }
         __syncthreads();  // the weight tile is reused by the next unit
     }
@@ -343,13 +377,31 @@ hipError_t launch_update_tokens_ring(const TokensParams &p, StateLayout layout, 
                     (int64_t)p.l * p.st_l * 2 + 2 * kChPerWave < lim;
     if (v8) {
         const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
-        const int64_t units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
-        *kernel_name = silu ? "tokens_ring_v8<silu>" : "tokens_ring_v8<identity>";
-        if (p.bias != nullptr)
-            return silu ? launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_SILU, true>, p, tiles, units, kBlock, stream)
-                        : launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_IDENTITY, true>, p, tiles, units, kBlock, stream);
-        return silu ? launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_SILU, false>, p, tiles, units, kBlock, stream)
-                    : launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_IDENTITY, false>, p, tiles, units, kBlock, stream);
+        const bool two = ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
+        const int64_t rows_per_block = kWavesPerBlock * (two ? 2 : 1);
+        const int64_t units = ((int64_t)p.n + rows_per_block - 1) / rows_per_block * tiles;
+        const bool l3 = p.l == 3;
+#define DCCONV_TR_GO(R_, KP_, B_, L3_)                                                                          \
+    return silu ? launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_SILU, B_, R_, KP_, L3_>, p, tiles, units, kBlock,  \
+                                     stream)                                                                    \
+                : launch_tokens_ring(tokens_ring_v8<DCCONV_ACT_IDENTITY, B_, R_, KP_, L3_>, p, tiles, units,      \
+                                     kBlock, stream)
+#define DCCONV_TR_B(R_, KP_, L3_)              \
+    if (p.bias != nullptr) {                   \
+        DCCONV_TR_GO(R_, KP_, true, L3_);      \
+    } else {                                   \
+        DCCONV_TR_GO(R_, KP_, false, L3_);     \
+    }
+        if (two) {
+            *kernel_name = silu ? "tokens_ring_v8<silu,R=2>" : "tokens_ring_v8<identity,R=2>";
+            if (l3) { DCCONV_TR_B(2, 4, true) }
+            DCCONV_TR_B(2, 4, false)
+        }
+        *kernel_name = silu ? "tokens_ring_v8<silu,R=1>" : "tokens_ring_v8<identity,R=1>";
+        if (l3) { DCCONV_TR_B(1, 8, true) }
+        DCCONV_TR_B(1, 8, false)
+#undef DCCONV_TR_B
+#undef DCCONV_TR_GO
     }
     const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
     const int64_t units = (int64_t)p.n * tiles;

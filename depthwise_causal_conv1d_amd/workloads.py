@@ -79,6 +79,8 @@ EXTRA = [
          routing="none", T=4, weight_dist="uniform", seed=4, one_call=True),
     Spec("large_decode_ring", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
          routing="none", weight_dist="uniform", seed=4, layout="channel_last", ring=True),
+    Spec("large_decode_ring_4tok", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
+         routing="none", T=4, weight_dist="uniform", seed=4, layout="channel_last", ring=True, one_call=True),
 ]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
@@ -153,8 +155,8 @@ def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bo
     once (the history shifts, so all L values are rewritten), weight, bias, the
     output of every token, index table.  Padding rows read no x and no state.
 
-    With ``ring`` (circular-buffer state, one token) only the W-1 newest values
-    are read and one value per channel is written.
+    With ``ring`` (circular-buffer state) only the W-1 newest values are read
+    and the last min(tokens, L) tokens are written, one value per channel each.
 
     State read: in the compact layout a channel's L values are adjacent, so all L
     are read.  Channel-last keeps each history position in its own plane; a
@@ -163,10 +165,10 @@ def algorithmic_bytes(N: int, D: int, W: int, L: int, active_rows: int, bias: bo
     L - min(tokens, L - (W-1)) planes are read (max(W-1, L-1) for one token)."""
     A, T = active_rows, tokens
     if ring:
-        # circular buffer (one token): the W-1 newest values read, one value per
-        # channel written, plus the count table
-        return (2 * A * D + 2 * A * D * (W - 1) + 2 * A * D + 2 * D * W + (2 * D if bias else 0)
-                + 2 * N * D + (4 * N if indices else 0) + 4 * N)
+        # circular buffer: the W-1 newest values read once, the last min(T, L)
+        # tokens written, plus the count table
+        return (2 * A * D * T + 2 * A * D * (W - 1) + 2 * A * D * min(T, L) + 2 * D * W + (2 * D if bias else 0)
+                + 2 * N * D * T + (4 * N if indices else 0) + 4 * N)
     read_positions = L if layout == "compact" else L - min(T, L - (W - 1))
     return (2 * A * D * T + 2 * A * D * read_positions + 2 * A * D * L + 2 * D * W
             + (2 * D if bias else 0) + 2 * N * D * T + (4 * N if indices else 0))

@@ -121,3 +121,9 @@ def test_cpu_baseline_ring_leg():
                     layout="channel_last", ring=True, seed=4)
     res = bench.cpu_baseline(small, wl.make(small), seconds=0.0)
     assert res["value"] > 0 and spec.ring
+
+
+def test_ring_tokens_bytes_by_hand():
+    N, D, T, L = 256, 8192, 4, 3
+    hand = 2 * N * D * T + 2 * N * D * 3 + 2 * N * D * min(T, L) + 2 * N * D * T + 2 * D * 4 + 4 * N
+    assert wl.algorithmic_bytes(N, D, 4, L, N, False, False, "channel_last", T, ring=True) == hand

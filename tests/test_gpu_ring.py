@@ -251,7 +251,7 @@ def test_ring_tokens(layout, L, T):
         got_state = got_state.transpose(0, 2, 1)
     np.testing.assert_array_equal(got_state, ref_state, err_msg="ring not bit-exact")
     assert_outputs_match(from_dev(out.permute(0, 2, 1)), ref, ref32)
-    assert kernel == ("tokens_ring_v8<silu>" if layout == "channel_last" else "tokens_ring_scalar<silu>"), kernel
+    assert kernel == ("tokens_ring_v8<silu,R=1>" if layout == "channel_last" else "tokens_ring_scalar<silu>"), kernel
 
 
 def test_ring_tokens_equal_single_ring_steps_on_gpu():
@@ -289,3 +289,27 @@ def test_ring_tokens_bad_count_rejects_row():
     assert int(stat.item()) == dc.DCCONV_DEV_BAD_SEQLEN
     assert np.all(wl.bf16_bits_to_f32(from_dev(out.permute(0, 2, 1))[1]) == 0)
     np.testing.assert_array_equal(from_dev(sd)[1], st[1])
+
+
+@pytest.mark.parametrize("L,T", [(3, 3), (3, 6), (4, 9)])
+def test_ring_tokens_two_rows_per_wave(L, T):
+    """Enough rows for two per wave (odd N, a padding row, bias), partial passes."""
+    rng = np.random.default_rng(3900 + 10 * L + T)
+    N, D, S = 129, 8192, 140
+    x = _bf(rng, (N, T, D)); w = _bf(rng, (D, 4)); b = _bf(rng, (D,), 0.1)
+    st = _bf(rng, (S, D, L))
+    idx = rng.choice(S, N, replace=False).astype(np.int32)
+    idx[7] = -1
+    seen = rng.integers(0, 1000, size=N).astype(np.int32)
+    ref_state = st.copy()
+    ref, ref32 = _ring_tokens_reference(x, ref_state, w, b, idx, seen, "silu")
+    sb, sd = guarded_copy(np.ascontiguousarray(st.transpose(0, 2, 1)))
+    out = dc.causal_conv1d_update_tokens(to_dev(x).permute(0, 2, 1), sd.permute(0, 2, 1), to_dev(w), to_dev(b),
+                                         "silu", conv_state_indices=torch.from_numpy(idx).cuda(),
+                                         cache_seqlens=torch.from_numpy(seen).cuda())
+    kernel = dc.dcconv_last_kernel()
+    torch.cuda.synchronize()
+    assert_guards_intact(sb)
+    np.testing.assert_array_equal(from_dev(sd).transpose(0, 2, 1), ref_state, err_msg="ring not bit-exact")
+    assert_outputs_match(from_dev(out.permute(0, 2, 1)), ref, ref32)
+    assert kernel == "tokens_ring_v8<silu,R=2>", kernel
