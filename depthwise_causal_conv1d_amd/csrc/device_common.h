@@ -24,21 +24,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Single-use streams: non-temporal 16-byte accesses.
-__device__ __forceinline__ u32x4 load_stream(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-__device__ __forceinline__ void store_stream(void *p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-// Reused data (weights, bias): ordinary cached loads.
-__device__ __forceinline__ u32x4 load_cached(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
 // Raw buffer accesses: a descriptor holds a base address and a byte count, and
 // the hardware turns any access at or beyond the count into a zero read or a
 // dropped write.  Word 3 is the gfx9 raw-buffer format (32-bit data format).
 typedef __amdgpu_buffer_rsrc_t Buffer;
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policies: single-use streams (x, state, out) carry the non-temporal
+// hint, which keeps them out of the Infinity Cache and from displacing reused
+// data; weights and bias use the default policy.
 constexpr int kCached = 0;  // cache policy: default
 constexpr int kStream = 2;  // cache policy: non-temporal
 __device__ __forceinline__ Buffer make_buffer(const void *base, uint32_t bytes) {

@@ -332,11 +332,11 @@ __global__ __launch_bounds__(kScalarBlock) void update_scalar(UpdateParams p, in
     }
 }
 
+// Launches `units` block units (the kernels stride over them when the grid is capped).
 template <typename Kernel>
-hipError_t launch(Kernel kernel, const UpdateParams &p, int tiles_per_row, int64_t units, int units_per_block,
-                  int block, hipStream_t stream) {
-    int64_t blocks = (units + units_per_block - 1) / units_per_block;
-    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+hipError_t launch(Kernel kernel, const UpdateParams &p, int tiles_per_row, int64_t units, int block,
+                  hipStream_t stream) {
+    const int64_t blocks = units < kMaxBlocks ? units : kMaxBlocks;
     UpdateParams args_p = p;
     void *args[] = {&args_p, &tiles_per_row, &units};
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks), dim3(block), args, 0,
@@ -351,13 +351,13 @@ hipError_t launch_compact_l(const UpdateParams &p, int tiles, hipStream_t stream
     if (p.n >= 2 && groups_two * tiles >= kMinWavesForTwoRows) {
         *name = name_two_rows;
         const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
-        return bias ? launch(update_compact_v8<L, ACT, 2, true>, p, tiles, block_units, 1, kBlock, stream)
-                    : launch(update_compact_v8<L, ACT, 2, false>, p, tiles, block_units, 1, kBlock, stream);
+        return bias ? launch(update_compact_v8<L, ACT, 2, true>, p, tiles, block_units, kBlock, stream)
+                    : launch(update_compact_v8<L, ACT, 2, false>, p, tiles, block_units, kBlock, stream);
     }
     *name = name_one_row;
     const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
-    return bias ? launch(update_compact_v8<L, ACT, 1, true>, p, tiles, block_units, 1, kBlock, stream)
-                : launch(update_compact_v8<L, ACT, 1, false>, p, tiles, block_units, 1, kBlock, stream);
+    return bias ? launch(update_compact_v8<L, ACT, 1, true>, p, tiles, block_units, kBlock, stream)
+                : launch(update_compact_v8<L, ACT, 1, false>, p, tiles, block_units, kBlock, stream);
 }
 
 template <int ACT>
@@ -397,13 +397,13 @@ hipError_t launch_channel_last_l(const UpdateParams &p, int tiles, hipStream_t s
     if (p.n >= 2 && groups_two * tiles >= kMinWavesForTwoRows) {
         *name = name_two_rows;
         const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
-        return bias ? launch(update_channel_last_v8<L, ACT, 2, true>, p, tiles, block_units, 1, kBlock, stream)
-                    : launch(update_channel_last_v8<L, ACT, 2, false>, p, tiles, block_units, 1, kBlock, stream);
+        return bias ? launch(update_channel_last_v8<L, ACT, 2, true>, p, tiles, block_units, kBlock, stream)
+                    : launch(update_channel_last_v8<L, ACT, 2, false>, p, tiles, block_units, kBlock, stream);
     }
     *name = name_one_row;
     const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
-    return bias ? launch(update_channel_last_v8<L, ACT, 1, true>, p, tiles, block_units, 1, kBlock, stream)
-                : launch(update_channel_last_v8<L, ACT, 1, false>, p, tiles, block_units, 1, kBlock, stream);
+    return bias ? launch(update_channel_last_v8<L, ACT, 1, true>, p, tiles, block_units, kBlock, stream)
+                : launch(update_channel_last_v8<L, ACT, 1, false>, p, tiles, block_units, kBlock, stream);
 }
 
 template <int ACT>
@@ -456,8 +456,8 @@ hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activati
     const int tiles = (p.d + kScalarBlock - 1) / kScalarBlock;
     const int64_t units = (int64_t)p.n * tiles;
     *kernel_name = silu ? "update_scalar<silu>" : "update_scalar<identity>";
-    return silu ? launch(update_scalar<DCCONV_ACT_SILU>, p, tiles, units, 1, kScalarBlock, stream)
-                : launch(update_scalar<DCCONV_ACT_IDENTITY>, p, tiles, units, 1, kScalarBlock, stream);
+    return silu ? launch(update_scalar<DCCONV_ACT_SILU>, p, tiles, units, kScalarBlock, stream)
+                : launch(update_scalar<DCCONV_ACT_IDENTITY>, p, tiles, units, kScalarBlock, stream);
 }
 
 }  // namespace dcconv
