@@ -122,6 +122,71 @@ __device__ __forceinline__ void chunk_piece(const PrefillParams &p, int i, int j
     }
 }
 
+// The packed form: outputs of packed tokens [q0, q1).  A token's history is
+// the three packed tokens before it whenever it is at least three tokens into
+// its sequence, so the window rolls over the packed stream across sequence
+// boundaries and the x loads are issued before the sequence table is read; the
+// table only decides which outputs are stored (those at least three tokens
+// into their sequence; the edge blocks write the first three) and which are
+// zero (padding or rejected sequences).  A table that is not ordered stops the
+// stores and sets DCCONV_DEV_BAD_SEQ; every access stays in bounds.
+template <int ACT>
+__device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int q1, int c0, uint32_t vec_bytes,
+                                             uint32_t lane_off, int lane, const float (&wf)[32],
+                                             const float (&bf)[8]) {
+    const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u;
+    const int qb = max(q0 - 3, 0);
+    const Buffer xbuf = make_buffer(p.x + (int64_t)qb * p.xs_t + c0, x_tok * (uint32_t)(q1 - 1 - qb) + vec_bytes);
+    const Buffer obuf = make_buffer(p.out + (int64_t)q0 * p.os_t + c0, o_tok * (uint32_t)(q1 - 1 - q0) + vec_bytes);
+    auto xoff = [&](int q) -> uint32_t {
+        return ((q >= qb && q < q1) ? x_tok * (uint32_t)(q - qb) : kBadToken) + lane_off;
+    };
+    u32x4 h0 = buffer_load<kStream>(xbuf, xoff(q0 - 3));
+    u32x4 h1 = buffer_load<kStream>(xbuf, xoff(q0 - 2));
+    u32x4 h2 = buffer_load<kStream>(xbuf, xoff(q0 - 1));
+    u32x4 cur[kPass];
+#pragma unroll
+    for (int k = 0; k < kPass; ++k) cur[k] = buffer_load<kStream>(xbuf, xoff(q0 + k));
+
+    // the sequence holding q0: its first token a, its end e, and its routing
+    int i = find_seq(p.starts, p.n, q0, lane), a = 0, e = 0;
+    bool ok = false, live = false;
+    auto enter = [&](int next) {
+        i = next;
+        ok = i >= 0 && i < p.n;
+        if (ok) {
+            a = p.starts[i];
+            e = p.starts[i + 1];
+            ok = a >= 0 && a <= e && e <= p.t;
+            if (!ok && p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
+        }
+        live = ok && route_row(p.idx, p.status, p.n, p.s, i, lane) >= 0;
+    };
+    enter(i);
+    for (int qq = q0; qq < q1; qq += kPass) {
+        u32x4 nxt[kPass];
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) nxt[k] = buffer_load<kStream>(xbuf, xoff(qq + kPass + k));
+        u32x4 ov[kPass];
+        uint32_t off[kPass];
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) {
+            const int q = qq + k;
+            const u32x4 y = conv8<ACT>(h0, h1, h2, cur[k], wf, bf);
+            h0 = h1;
+            h1 = h2;
+            h2 = cur[k];
+            while (ok && q < q1 && q >= e) enter(i + 1);  // past the end of this (or an empty) sequence
+            ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};
+            off[k] = ((ok && q < q1 && q - a >= 3) ? o_tok * (uint32_t)(q - q0) : kBadToken) + lane_off;
+        }
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) buffer_store<kStream>(ov[k], obuf, off[k]);
+#pragma unroll
+        for (int k = 0; k < kPass; ++k) cur[k] = nxt[k];
+    }
+}
+
 // One block of the chunk role: virtual block vb of v_blocks (a multiple of 8).
 template <int ACT, bool HAS_BIAS>
 __device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weight_tile, int tiles, int chunk,
@@ -160,27 +225,9 @@ __device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weigh
                 chunk_piece<ACT>(p, i, j0, j1, p.x + (int64_t)i * p.xs_n, p.out + (int64_t)i * p.os_n, c0, vec_bytes,
                                  lane_off, lane, wf, bf);
             } else {
-                // packed form: the unit is packed tokens [q, q1), cut at sequence boundaries
-                int q = (int)unit * chunk;
-                const int q1 = min(p.t, q + chunk);
-                int i = find_seq(p.starts, p.n, q, lane);
-                while (q < q1) {  // each pass advances q or i; i is bounded by n
-                    if (i < 0 || i >= p.n) break;
-                    const int a = p.starts[i], e = p.starts[i + 1];
-                    if (e <= q && e >= a) {  // an empty sequence at q
-                        ++i;
-                        continue;
-                    }
-                    if (a < 0 || a > q || e < a || e > p.t) {  // not an ordered table: unspecified, stay in bounds
-                        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
-                        break;
-                    }
-                    const int qe = min(q1, e);
-                    chunk_piece<ACT>(p, i, q - a, qe - a, p.x + (int64_t)a * p.xs_t, p.out + (int64_t)a * p.os_t, c0,
-                                     vec_bytes, lane_off, lane, wf, bf);
-                    q = qe;
-                    ++i;
-                }
+                // packed form: the unit is packed tokens [q0, q1)
+                const int q0 = (int)unit * chunk;
+                chunk_packed<ACT>(p, q0, min(p.t, q0 + chunk), c0, vec_bytes, lane_off, lane, wf, bf);
             }
         }
         __syncthreads();  // the weight tile is reused by the next block unit
