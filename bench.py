@@ -113,6 +113,7 @@ class Workload:
                 out=torch.empty(spec.N, self.tokens, spec.D, dtype=torch.bfloat16, device=dev)))
         self.set_bytes = set_bytes
         active = spec.N if data["indices"] is None else int((data["indices"] >= 0).sum())
+        self.active = active  # rows with a slot (the rest are padding)
         self.bytes_per_call = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active,
                                                    data["bias"] is not None, data["indices"] is not None,
                                                    spec.layout, self.tokens, spec.ring)
@@ -234,6 +235,8 @@ def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
                tokens_per_call=wk.tokens,
                buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
     res["frac"] = res["gbs"] / PEAK_HBM_GBS
+    if getattr(wk, "active", spec.N) != spec.N:
+        res["active_rows_per_s"] = wk.active * wk.tokens / (ms * 1e-3)
     host = wk.host
     del wk
     torch.cuda.empty_cache()
@@ -461,7 +464,7 @@ def main():
                 f"{r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}")
             entry = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
                      if k in ("workload", "kernel", "us_per_call", "gbs", "frac", "rows_per_s",
-                              "bytes_per_call", "tokens_per_call")}
+                              "active_rows_per_s", "bytes_per_call", "tokens_per_call")}
             entry["traffic"] = read_traffic(r["kernel"], other.name)
             others.append(entry)
     cpu = None
