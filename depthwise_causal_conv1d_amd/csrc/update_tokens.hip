@@ -9,14 +9,21 @@
 // once instead of T times: per active channel-row the bytes drop from
 // T * (4 + 4L) + 2T to 4L + 4T (compact layout).
 //
-//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP>: one wavefront owns R rows
-//    of one 512-channel tile (8 channels per lane), the block shares the tile's
-//    weights.
+//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP, SPLIT>: one wavefront owns
+//    R rows of one 512-channel tile (8 channels per lane), the block shares the
+//    tile's weights.  With SPLIT (one row per block, T >= 2L) the block's two
+//    waves share one row and split its tokens at h = T/2: outputs from token 3
+//    on depend on x alone, so wave 1 starts from the three tokens before h,
+//    produces outputs [h, T) and writes the final state (with T >= 2L it holds
+//    tokens of that half only), while wave 0 reads the state and produces
+//    outputs [0, h).  That doubles the waves of a thin grid (few rows, long
+//    calls) and halves each wave's dependent chain.
 //    The history lives in registers in plane-major form (one 16-byte vector per
 //    history position, 8 channels each), so a token's shift is a renaming of
 //    registers.  Tokens go in passes of KP: the pass's x vectors are all loaded
-//    before the first is used and its outputs are all stored after the last
-//    is computed.  Compact state goes through the same LDS stage as the
+//    before the first is used (the next pass's loads are issued before this
+//    pass is computed) and its outputs are all stored after the last is
+//    computed.  Compact state goes through the same LDS stage as the
 //    single-token kernel; channel-last state is already plane-major.
 //  * tokens_scalar<ACT>: one thread per (row, channel), any strides, any L >= 3;
 //    each token is one single-step update of the thread's channel in memory.
@@ -35,8 +42,9 @@ namespace {
 constexpr uint32_t kBadToken = 1u << 30;
 constexpr uint32_t kBadLane = 1u << 31;
 
-template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP>
+template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_per_row, int64_t block_units) {
+    static_assert(!SPLIT || R == 1, "a split block holds one row");
     __shared__ u32x4 stage_all[kWavesPerBlock][CHANNEL_LAST ? 1 : kWave * L];
     __shared__ u32x4 weight_tile[4 * kWave];
     // Positions read in the channel-last layout: the first token's taps need
@@ -47,10 +55,15 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
 
-    // A block owns one 512-channel tile and kWavesPerBlock groups of R rows.
+    // A block owns one 512-channel tile and kWavesPerBlock groups of R rows, or
+    // with SPLIT one row whose tokens [tb, te) are this wave's share.
+    const int tb = (SPLIT && wave == 1) ? p.t / 2 : 0;
+    const int te = (SPLIT && wave == 0) ? p.t / 2 : p.t;
+    const bool reads_state = !SPLIT || wave == 0;
+    const bool writes_state = !SPLIT || wave == 1;
     for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
         const int tile = (int)(bu % tiles_per_row);
-        const int group = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
+        const int group = SPLIT ? (int)(bu / tiles_per_row) : (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
@@ -63,41 +76,60 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
         }
 
         // every load of the first pass up front: weights, bias, each row's
-        // state and its first KP tokens
+        // state (or, for the second half of a split row, the three tokens
+        // before it) and its first KP tokens
         __builtin_amdgcn_s_setprio(3);
         u32x4 wraw[kWeightChunks];
         weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
         Buffer sbuf[R], xbuf[R], obuf[R];
-        u32x4 sv[R][L], xv[R][KP];
+        u32x4 sv[R][L], xv[R][KP], hx[3];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const bool live = slot[r] >= 0;
             const int row = min(group * R + r, p.n - 1);
+            // x and out of this row: one descriptor each, spanning every token
+            xbuf[r] = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+            obuf[r] = make_buffer(p.out + (int64_t)row * p.os_n + c0,
+                                  slot[r] != -2 ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
             // State: compact = the tile's contiguous run of L KiB, read coalesced;
             // channel-last = planes kFirst..L-1 of this tile.
             if (CHANNEL_LAST) {
                 sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + c0 : p.x,
                                       live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
+                // The second half of a split row takes the three tokens before
+                // its first as the three newest positions and zeros below them
+                // (an empty descriptor): one load sequence for both halves.
+                const Buffer older = reads_state ? sbuf[r] : make_buffer(p.x, 0u);
+                const Buffer newest = reads_state ? sbuf[r] : xbuf[r];
 #pragma unroll
-                for (int k = 0; k < L; ++k)
-                    sv[r][k] = k < kFirst ? u32x4{0u, 0u, 0u, 0u}
-                                          : buffer_load<kStream>(sbuf[r], plane_bytes * (uint32_t)k + lane_off);
+                for (int k = 0; k < L; ++k) {
+                    if (k < kFirst)
+                        sv[r][k] = u32x4{0u, 0u, 0u, 0u};
+                    else if (k < L - 3)
+                        sv[r][k] = buffer_load<kStream>(older, plane_bytes * (uint32_t)k + lane_off);
+                    else
+                        sv[r][k] = buffer_load<kStream>(
+                            newest,
+                            (reads_state ? plane_bytes * (uint32_t)k : x_tok * (uint32_t)(tb - L + k)) + lane_off);
+                }
             } else {
                 sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + (int64_t)c0 * L : p.x,
                                       live ? vec_bytes * L : 0u);
+                if (reads_state) {
 #pragma unroll
-                for (int j = 0; j < L; ++j)
-                    sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+                    for (int j = 0; j < L; ++j)
+                        sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+                }
             }
-            // x and out of this row: one descriptor each, spanning every token
-            xbuf[r] = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
-            obuf[r] = make_buffer(p.out + (int64_t)row * p.os_n + c0,
-                                  slot[r] != -2 ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+            if (!CHANNEL_LAST && !reads_state) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) hx[k] = buffer_load<kStream>(xbuf[r], x_tok * (uint32_t)(tb - 3 + k) + lane_off);
+            }
 #pragma unroll
             for (int i = 0; i < KP; ++i)
-                xv[r][i] = buffer_load<kStream>(xbuf[r], (i < p.t ? x_tok * (uint32_t)i : kBadToken) + lane_off);
+                xv[r][i] = buffer_load<kStream>(xbuf[r], (tb + i < te ? x_tok * (uint32_t)(tb + i) : kBadToken) + lane_off);
         }
         __builtin_amdgcn_s_setprio(0);
 
@@ -111,6 +143,13 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
             if (CHANNEL_LAST) {
 #pragma unroll
                 for (int k = 0; k < L; ++k) pl[r][k] = sv[r][k];
+            } else if (!reads_state) {
+                // the second half of a split row: only the three newest
+                // positions matter (the T - h >= L tokens ahead shift out the rest)
+#pragma unroll
+                for (int k = 0; k < L - 3; ++k) pl[r][k] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int k = 0; k < 3; ++k) pl[r][L - 3 + k] = hx[k];
             } else {
                 u32x4 *stage = stage_all[wave];
                 wave_lds_sync();
@@ -128,16 +167,30 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
             }
         }
 
-        for (int t0 = 0; t0 < p.t; t0 += KP) {
-            if (t0 > 0) {
+        // A split row's state is read by wave 0 and rewritten by wave 1.  The
+        // empty asm consumes the loaded state, so wave 0's loads have returned
+        // before the barrier and wave 1's write, after it, cannot overtake them.
+        if (SPLIT) {
+            if (reads_state) {
+#pragma unroll
+                for (int k = 0; k < L; ++k) asm volatile("" ::"v"(sv[0][k]));
+            }
+            __syncthreads();
+        }
+
+        for (int t0 = tb; t0 < te; t0 += KP) {
+            // the next pass's x is loaded before this pass is computed, so its
+            // latency runs under this pass's arithmetic and stores
+            u32x4 xn[R][KP];
+            if (t0 + KP < te) {  // wave-uniform
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int i = 0; i < KP; ++i)
-                        xv[r][i] = buffer_load<kStream>(
-                            xbuf[r], (t0 + i < p.t ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+                        xn[r][i] = buffer_load<kStream>(
+                            xbuf[r], (t0 + KP + i < te ? x_tok * (uint32_t)(t0 + KP + i) : kBadToken) + lane_off);
             }
-            const int tokens = min(KP, p.t - t0);
+            const int tokens = min(KP, te - t0);
             u32x4 ov[R][KP];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -162,12 +215,18 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
 #pragma unroll
                 for (int i = 0; i < KP; ++i)
                     buffer_store<kStream>(ov[r][i], obuf[r],
-                                          (t0 + i < p.t ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+                                          (t0 + i < te ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
+            if (t0 + KP < te) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < KP; ++i) xv[r][i] = xn[r][i];
+            }
         }
 
-        // Write the final history back.
+        // Write the final history back (a split row's second half holds it).
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < R && writes_state; ++r) {
             if (CHANNEL_LAST) {
 #pragma unroll
                 for (int k = 0; k < L; ++k) buffer_store<kStream>(pl[r][k], sbuf[r], plane_bytes * (uint32_t)k + lane_off);
@@ -239,33 +298,45 @@ hipError_t launch_tokens(Kernel kernel, const TokensParams &p, int tiles_per_row
                            stream);
 }
 
-template <int L, int ACT, bool CL, int R, int KP>
+template <int L, int ACT, bool CL, int R, int KP, bool SPLIT = false>
 hipError_t launch_tokens_l(const TokensParams &p, int tiles, hipStream_t stream) {
-    const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock * R - 1) / (kWavesPerBlock * R));
-    return p.bias != nullptr ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP>, p, tiles, block_units, kBlock, stream)
-                             : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP>, p, tiles, block_units, kBlock, stream);
+    const int64_t rows_per_block = SPLIT ? 1 : kWavesPerBlock * R;
+    const int64_t block_units = tiles * (((int64_t)p.n + rows_per_block - 1) / rows_per_block);
+    return p.bias != nullptr
+               ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP, SPLIT>, p, tiles, block_units, kBlock, stream)
+               : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP, SPLIT>, p, tiles, block_units, kBlock, stream);
 }
+
+// A grid of one row per wave below this many waves (under two per SIMD) splits
+// each row's tokens over two waves when the call is long enough (T >= 2L).
+constexpr int64_t kMaxWavesForSplit = 2048;
 
 template <int ACT, bool CL>
 hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream, const char **name) {
-    // Two rows per wave (4 tokens per pass, to bound registers) when the
-    // history is short and the grid still fills the chip with them; else one
-    // row and 8 tokens per pass.
+    // Two rows per wave when the history is short and the grid still fills the
+    // chip with them; else one row per wave, its tokens split over two waves
+    // when the grid is thin and the call long.  Passes of 4 tokens (with the
+    // next pass in flight) keep every form within 256 registers.
     const bool two = p.l <= 4 && ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
-#define DCCONV_TOK_NAME(LL, RR)                                                              \
-    (CL ? (ACT ? "tokens_v8<L=" #LL ",silu,channel_last,R=" #RR ">"                         \
-               : "tokens_v8<L=" #LL ",identity,channel_last,R=" #RR ">")                    \
-        : (ACT ? "tokens_v8<L=" #LL ",silu,compact,R=" #RR ">" : "tokens_v8<L=" #LL ",identity,compact,R=" #RR ">"))
-#define DCCONV_TOK_CASE(LL)                                       \
-    case LL:                                                      \
-        *name = DCCONV_TOK_NAME(LL, 1);                           \
-        return launch_tokens_l<LL, ACT, CL, 1, 8>(p, tiles, stream);
+    const bool split = !two && (int64_t)p.n * tiles < kMaxWavesForSplit && p.t >= 2 * p.l;
+#define DCCONV_TOK_NAME(LL, SUF)                                                              \
+    (CL ? (ACT ? "tokens_v8<L=" #LL ",silu,channel_last," SUF ">"                            \
+               : "tokens_v8<L=" #LL ",identity,channel_last," SUF ">")                       \
+        : (ACT ? "tokens_v8<L=" #LL ",silu,compact," SUF ">" : "tokens_v8<L=" #LL ",identity,compact," SUF ">"))
+#define DCCONV_TOK_CASE(LL)                                                    \
+    case LL:                                                                   \
+        if (split) {                                                           \
+            *name = DCCONV_TOK_NAME(LL, "R=1,split");                          \
+            return launch_tokens_l<LL, ACT, CL, 1, 4, true>(p, tiles, stream); \
+        }                                                                      \
+        *name = DCCONV_TOK_NAME(LL, "R=1");                                    \
+        return launch_tokens_l<LL, ACT, CL, 1, 4>(p, tiles, stream);
     if (two) {
         if (p.l == 3) {
-            *name = DCCONV_TOK_NAME(3, 2);
+            *name = DCCONV_TOK_NAME(3, "R=2");
             return launch_tokens_l<3, ACT, CL, 2, 4>(p, tiles, stream);
         }
-        *name = DCCONV_TOK_NAME(4, 2);
+        *name = DCCONV_TOK_NAME(4, "R=2");
         return launch_tokens_l<4, ACT, CL, 2, 4>(p, tiles, stream);
     }
     switch (p.l) {

@@ -121,20 +121,27 @@ class TokensCase:
 # ------------------------------------------------------------------ vector path
 
 
+def _one_row_form(T, L):
+    """Kernel-name suffix of the one-row form on a thin grid: a call of at least
+    2L tokens splits each row's tokens over two waves."""
+    return "R=1,split>" if T >= 2 * L else "R=1>"
+
+
 @pytest.mark.parametrize("L", [3, 4, 8])
 @pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 16, 33])
 def test_tokens_compact(L, T):
     case = TokensCase(1000 + 10 * L + T, N=6, D=1096, T=T, L=L, bias=T % 2 == 1,
                       act="silu" if T % 3 else None)
     case.check()
-    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("compact,R=1>"), case.kernel
+    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("compact," + _one_row_form(T, L)), \
+        case.kernel
 
 
 @pytest.mark.parametrize("L", [5, 6, 7])
 def test_tokens_compact_other_history_lengths(L):
     case = TokensCase(1100 + L, N=5, D=520, T=11, L=L, bias=True, act="silu", routing="unique", S=9)
     case.check()
-    assert case.kernel == f"tokens_v8<L={L},silu,compact,R=1>", case.kernel
+    assert case.kernel == f"tokens_v8<L={L},silu,compact," + _one_row_form(11, L), case.kernel
 
 
 @pytest.mark.parametrize("L", [3, 4, 5, 6, 7, 8])
@@ -143,7 +150,8 @@ def test_tokens_channel_last(L, T):
     case = TokensCase(1200 + 10 * L + T, N=7, D=1608, T=T, L=L, layout="channel_last", bias=L % 2 == 0,
                       act="silu" if T != 4 else None, routing="unique", S=11)
     case.check()
-    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("channel_last,R=1>"), case.kernel
+    assert case.kernel.startswith(f"tokens_v8<L={L},") and case.kernel.endswith("channel_last," + _one_row_form(T, L)), \
+        case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
@@ -166,7 +174,7 @@ def test_tokens_long_history_in_one_call():
     case.indices = case.oracle_indices = data["indices"]
     case.act, case.layout, case.out_layout, case.status = spec.act, spec.layout, "token_major", True
     assert case.check() == 0
-    assert case.kernel == "tokens_v8<L=8,identity,compact,R=1>", case.kernel
+    assert case.kernel == "tokens_v8<L=8,identity,compact,R=1,split>", case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
@@ -187,6 +195,27 @@ def test_tokens_two_rows_per_wave(layout, T):
                       S=160, status=True)
     assert case.check() == 0
     assert case.kernel == f"tokens_v8<L=4,silu,{layout},R=2>", case.kernel
+
+
+@pytest.mark.parametrize("layout", ["compact", "channel_last"])
+@pytest.mark.parametrize("L,T", [(3, 6), (3, 7), (4, 8), (8, 16), (8, 17), (6, 33)])
+def test_tokens_split_rows(layout, L, T):
+    """Thin grid, long call: each row's tokens split over the block's two waves
+    (the first reads the state, the second starts from the three tokens before
+    its half and writes the final state).  Ragged last tile, padding rows, a
+    status word, bias, T = 2L exactly and odd T."""
+    case = TokensCase(2300 + 10 * L + T, N=10, D=1096, T=T, L=L, layout=layout, bias=True, routing="padded",
+                      n_pad=3, S=14, status=True, act="silu" if T % 2 else None)
+    assert case.check() == 0
+    assert case.kernel == f"tokens_v8<L={L},{'silu' if T % 2 else 'identity'},{layout},R=1,split>", case.kernel
+
+
+def test_tokens_one_row_full_grid_does_not_split():
+    """A grid of one row per wave that already holds two waves per SIMD keeps
+    each row on one wave (L > 4 rules out two rows per wave)."""
+    case = TokensCase(2400, N=129, D=8192, T=11, L=5, bias=True, routing="padded", n_pad=5, S=140, status=True)
+    assert case.check() == 0
+    assert case.kernel == "tokens_v8<L=5,silu,compact,R=1>", case.kernel
 
 
 # ---------------------------------------------------------- routing and padding
@@ -278,11 +307,13 @@ def test_tokens_zero_tokens_leave_everything():
     np.testing.assert_array_equal(from_dev(sd), st)
 
 
-def test_tokens_in_hip_graph_replays():
+@pytest.mark.parametrize("T", [5, 9])
+def test_tokens_in_hip_graph_replays(T):
     """A captured multi-token call, replayed with fresh tokens each time (copied
-    in eagerly between replays), matches the oracle stepping the same way."""
-    rng = np.random.default_rng(2200)
-    N, D, T, L = 64, 2048, 5, 4
+    in eagerly between replays), matches the oracle stepping the same way
+    (T = 9 takes the split form)."""
+    rng = np.random.default_rng(2200 + T)
+    N, D, L = 64, 2048, 4
     st_h = _bf(rng, (N, D, L)); w_h = _bf(rng, (D, 4)); b_h = _bf(rng, (D,), 0.1)
     sd, wd, bd = to_dev(st_h), to_dev(w_h), to_dev(b_h)
     xbuf = torch.empty(N, T, D, dtype=torch.bfloat16, device="cuda")
