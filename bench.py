@@ -429,7 +429,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the decode "
-              "update needs no communication and this build runs on a single MI355X.", file=sys.stderr)
+              "update needs no communication, and a multi-GPU deployment runs one process per GPU on its "
+              "own share of the channels.", file=sys.stderr)
         sys.exit(2)
 
     import torch
