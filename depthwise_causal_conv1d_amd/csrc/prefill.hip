@@ -15,11 +15,10 @@
 //    neighbouring chunks of one tile and share its weights.  The chunk length
 //    is set per call so that about 8 waves per CU each stream one long run (a
 //    single resident round; 128 tokens for 8 x 2048 tokens at D = 8192).  A
-//    chunk re-reads the 3 tokens before it (its halo); with short chunks the
-//    blocks are mapped so that each XCD walks a contiguous run of chunks, where
-//    the halo is the neighbour's data in that XCD's L2.  Tokens go in passes of
-//    4, double buffered: the next pass's loads are issued before the current
-//    pass is computed and stored.
+//    chunk re-reads the 3 tokens before it (its halo).  Blocks go in plain
+//    order, the tile varying fastest.  Tokens go in passes of 4, double
+//    buffered: the next pass's loads are issued before the current pass is
+//    computed and stored.
 //  * edge blocks: everything that touches a slot -- the first min(3, T)
 //    outputs, which read the initial state, and the final state, which
 //    replaces it -- one wavefront per (sequence, tile), so each slot is read
@@ -45,7 +44,6 @@ constexpr int kMinChunk = 16;
 constexpr int kMaxChunk = 256;
 constexpr int64_t kTargetWaves = 2048;
 constexpr int kPass = 4;    // tokens per load pass
-constexpr int kXcds = 8;    // MI355X: workgroups go round-robin over 8 XCDs
 // Buffer offsets beyond every descriptor used here (all are below 2^30 bytes):
 // a token outside the piece, and a lane past a ragged tile.  Their sum and any
 // valid offset plus either stay below 2^32.
@@ -187,20 +185,15 @@ __device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int
     }
 }
 
-// One block of the chunk role: virtual block vb of v_blocks (a multiple of 8).
+// One block of the chunk role: block v of the chunk blocks, the (tile, pair of
+// chunks) with the tile varying fastest.
 template <int ACT, bool HAS_BIAS>
 __device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weight_tile, int tiles, int chunk,
-                                            int xcd_map, int64_t units, int64_t units_per_seq, int64_t n_blocks,
-                                            int64_t v_blocks, int64_t vb) {
+                                            int64_t units, int64_t units_per_seq, int64_t v) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
-    const int64_t per_xcd = v_blocks / kXcds;
     {
-        // workgroup vb runs on XCD vb % 8: with short chunks give each XCD a
-        // contiguous run of blocks (their halos are each other's data)
-        const int64_t v = xcd_map ? (vb % kXcds) * per_xcd + vb / kXcds : vb;
-        if (v >= n_blocks) return;  // block-uniform
         const int tile = (int)(v % tiles);
         const int64_t unit = (v / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -392,22 +385,19 @@ __device__ __forceinline__ void edge_block(const PrefillParams &p, u32x4 *stage_
 }
 
 // Both roles in one launch: the edge blocks first (they start before the long
-// chunk blocks and finish under them), then the chunk blocks.  edge_blocks is a
-// multiple of 8, so chunk block vb runs on XCD vb % 8.
+// chunk blocks and finish under them), then the chunk blocks.
 template <int L, int ACT, int LAYOUT, bool HAS_BIAS>
-__global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles, int chunk, int xcd_map,
-                                                     int64_t units, int64_t units_per_seq, int64_t n_blocks,
-                                                     int64_t v_blocks, int64_t edge_units, int64_t edge_blocks) {
+__global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles, int chunk, int64_t units,
+                                                     int64_t units_per_seq, int64_t chunk_blocks,
+                                                     int64_t edge_blocks) {
     __shared__ u32x4 stage_all[kWavesPerBlock * kWave * L];
     __shared__ u32x4 weight_tile[4 * kWave];
-    const int64_t total = edge_blocks + v_blocks;
+    const int64_t total = edge_blocks + chunk_blocks;
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
-        if (b < edge_blocks) {
-            if (b < edge_units) edge_block<L, ACT, LAYOUT>(p, stage_all, weight_tile, tiles, b);
-        } else {
-            chunk_block<ACT, HAS_BIAS>(p, weight_tile, tiles, chunk, xcd_map, units, units_per_seq, n_blocks, v_blocks,
-                                       b - edge_blocks);
-        }
+        if (b < edge_blocks)
+            edge_block<L, ACT, LAYOUT>(p, stage_all, weight_tile, tiles, b);
+        else
+            chunk_block<ACT, HAS_BIAS>(p, weight_tile, tiles, chunk, units, units_per_seq, b - edge_blocks);
     }
 }
 
@@ -491,20 +481,17 @@ hipError_t launch_prefill_l(const PrefillParams &p, int tiles, hipStream_t strea
     chunk = chunk < kMinChunk ? kMinChunk : chunk > kMaxChunk ? kMaxChunk : chunk;
     const int64_t units_per_seq = ((int64_t)p.t + chunk - 1) / chunk;
     const int64_t units = p.starts != nullptr ? units_per_seq : units_per_seq * p.n;
-    const int xcd_map = chunk < 64;
-    const int64_t n_blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
-    const int64_t v_blocks = (n_blocks + kXcds - 1) / kXcds * kXcds;
-    const int64_t edge_units = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
-    const int64_t edge_blocks = (edge_units + kXcds - 1) / kXcds * kXcds;
-    const int64_t total = edge_blocks + v_blocks;
-    const int64_t grid = total < kMaxBlocks ? total : kMaxBlocks;  // both multiples of 8
+    const int64_t chunk_blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+    const int64_t edge_blocks = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
+    const int64_t total = edge_blocks + chunk_blocks;
+    const int64_t grid = total < kMaxBlocks ? total : kMaxBlocks;
     PrefillParams pp = p;
     const int ch = (int)chunk;
     return p.bias != nullptr
-               ? launch(prefill_v8<L, ACT, LAYOUT, true>, grid, kBlock, stream, pp, tiles, ch, xcd_map, units,
-                        units_per_seq, n_blocks, v_blocks, edge_units, edge_blocks)
-               : launch(prefill_v8<L, ACT, LAYOUT, false>, grid, kBlock, stream, pp, tiles, ch, xcd_map, units,
-                        units_per_seq, n_blocks, v_blocks, edge_units, edge_blocks);
+               ? launch(prefill_v8<L, ACT, LAYOUT, true>, grid, kBlock, stream, pp, tiles, ch, units, units_per_seq,
+                        chunk_blocks, edge_blocks)
+               : launch(prefill_v8<L, ACT, LAYOUT, false>, grid, kBlock, stream, pp, tiles, ch, units, units_per_seq,
+                        chunk_blocks, edge_blocks);
 }
 
 template <int ACT, int LAYOUT>
