@@ -86,6 +86,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Element i of an int32 table the kernel never writes, for a wave-uniform i:
+// read through the constant address space, so it is a scalar load whose wait
+// does not drain the vector loads in flight (a plain load issued after a store
+// of the kernel cannot be proven unclobbered and becomes a vector load).
+__device__ __forceinline__ int32_t load_uniform(const int32_t *table, int i) {
+    return ((const __attribute__((address_space(4))) int32_t *)table)[i];
+}
+
 // Slot of `row`, or -1 when the row must not touch the state (a padding row, an
 // out-of-range index, or -- when a status word is given -- a slot another row of
 // the batch also selects).  idx/status may be null.  Must be called by all 64
@@ -93,7 +101,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ int route_row(const int32_t *idx, int32_t *status, int n_rows, int n_slots, int row,
                                          int lane) {
     if (idx == nullptr) return row;
-    const int slot = idx[row];
+    const int slot = load_uniform(idx, row);
     if (slot == -1) return -1;
     if (slot < -1 || slot >= n_slots) {
         if (status != nullptr && lane == 0) atomicOr(status, DCCONV_DEV_BAD_INDEX);

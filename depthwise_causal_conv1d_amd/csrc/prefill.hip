@@ -153,8 +153,8 @@ __device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int
         i = next;
         ok = i >= 0 && i < p.n;
         if (ok) {
-            a = p.starts[i];
-            e = p.starts[i + 1];
+            a = load_uniform(p.starts, i);
+            e = load_uniform(p.starts, i + 1);
             ok = a >= 0 && a <= e && e <= p.t;
             if (!ok && p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
         }
