@@ -167,16 +167,29 @@ __device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int
         for (int k = 0; k < kPass; ++k) nxt[k] = buffer_load<kStream>(xbuf, xoff(qq + kPass + k));
         u32x4 ov[kPass];
         uint32_t off[kPass];
+        if (ok && qq - a >= 3 && qq + kPass <= e && qq + kPass <= q1) {
+            // the common pass: inside one sequence, past its first three tokens
 #pragma unroll
-        for (int k = 0; k < kPass; ++k) {
-            const int q = qq + k;
-            const u32x4 y = conv8<ACT>(h0, h1, h2, cur[k], wf, bf);
-            h0 = h1;
-            h1 = h2;
-            h2 = cur[k];
-            while (ok && q < q1 && q >= e) enter(i + 1);  // past the end of this (or an empty) sequence
-            ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};
-            off[k] = ((ok && q < q1 && q - a >= 3) ? o_tok * (uint32_t)(q - q0) : kBadToken) + lane_off;
+            for (int k = 0; k < kPass; ++k) {
+                const u32x4 y = conv8<ACT>(h0, h1, h2, cur[k], wf, bf);
+                h0 = h1;
+                h1 = h2;
+                h2 = cur[k];
+                ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};
+                off[k] = o_tok * (uint32_t)(qq + k - q0) + lane_off;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPass; ++k) {
+                const int q = qq + k;
+                const u32x4 y = conv8<ACT>(h0, h1, h2, cur[k], wf, bf);
+                h0 = h1;
+                h1 = h2;
+                h2 = cur[k];
+                while (ok && q < q1 && q >= e) enter(i + 1);  // past the end of this (or an empty) sequence
+                ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};
+                off[k] = ((ok && q < q1 && q - a >= 3) ? o_tok * (uint32_t)(q - q0) : kBadToken) + lane_off;
+            }
         }
 #pragma unroll
         for (int k = 0; k < kPass; ++k) buffer_store<kStream>(ov[k], obuf, off[k]);
