@@ -21,9 +21,9 @@
 //    The history lives in registers in plane-major form (one 16-byte vector per
 //    history position, 8 channels each), so a token's shift is a renaming of
 //    registers.  Tokens go in passes of KP: the pass's x vectors are all loaded
-//    before the first is used (the next pass's loads are issued before this
-//    pass is computed) and its outputs are all stored after the last is
-//    computed.  Compact state goes through the same LDS stage as the
+//    before the first is used (with one row per wave, the next pass's loads
+//    are issued before this pass is computed) and its outputs are all stored
+//    after the last is computed.  Compact state goes through the same LDS stage as the
 //    single-token kernel; channel-last state is already plane-major.
 //  * tokens_scalar<ACT>: one thread per (row, channel), any strides, any L >= 3;
 //    each token is one single-step update of the thread's channel in memory.
@@ -178,17 +178,27 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
             __syncthreads();
         }
 
+        // One row per wave: the next pass's x is loaded before this pass is
+        // computed, so its latency runs under this pass's arithmetic and stores
+        // (a thin grid has no other wave on the SIMD to cover it).  Two rows
+        // per wave load each pass at its start and keep the registers.
+        constexpr bool kPrefetch = R == 1;
         for (int t0 = tb; t0 < te; t0 += KP) {
-            // the next pass's x is loaded before this pass is computed, so its
-            // latency runs under this pass's arithmetic and stores
             u32x4 xn[R][KP];
-            if (t0 + KP < te) {  // wave-uniform
+            if (kPrefetch && t0 + KP < te) {  // wave-uniform
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int i = 0; i < KP; ++i)
                         xn[r][i] = buffer_load<kStream>(
                             xbuf[r], (t0 + KP + i < te ? x_tok * (uint32_t)(t0 + KP + i) : kBadToken) + lane_off);
+            } else if (!kPrefetch && t0 > tb) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < KP; ++i)
+                        xv[r][i] = buffer_load<kStream>(
+                            xbuf[r], (t0 + i < te ? x_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
             }
             const int tokens = min(KP, te - t0);
             u32x4 ov[R][KP];
@@ -216,7 +226,7 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
                 for (int i = 0; i < KP; ++i)
                     buffer_store<kStream>(ov[r][i], obuf[r],
                                           (t0 + i < te ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
-            if (t0 + KP < te) {
+            if (kPrefetch && t0 + KP < te) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
