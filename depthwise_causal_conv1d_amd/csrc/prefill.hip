@@ -120,6 +120,31 @@ __device__ __forceinline__ void chunk_piece(const PrefillParams &p, int i, int j
     }
 }
 
+// A wave-uniform cursor over the packed sequence table: sequence i covers
+// packed tokens [a, e); ok is false past the table and for an entry that is not
+// ordered (which sets DCCONV_DEV_BAD_SEQ); live is ok and routed to a slot.
+struct SeqCursor {
+    int i = 0, a = 0, e = 0;
+    bool ok = false, live = false;
+
+    __device__ __forceinline__ void enter(const PrefillParams &p, int next, int lane) {
+        i = next;
+        ok = i >= 0 && i < p.n;
+        if (ok) {
+            a = load_uniform(p.starts, i);
+            e = load_uniform(p.starts, i + 1);
+            ok = a >= 0 && a <= e && e <= p.t;
+            if (!ok && p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
+        }
+        live = ok && route_row(p.idx, p.status, p.n, p.s, i, lane) >= 0;
+    }
+    // on to the sequence holding packed token q, past empty ones (ends at the
+    // table's end: every step moves i forward)
+    __device__ __forceinline__ void advance(const PrefillParams &p, int q, int lane) {
+        while (ok && q >= e) enter(p, i + 1, lane);
+    }
+};
+
 // The packed form: outputs of packed tokens [q0, q1).  A token's history is
 // the three packed tokens before it whenever it is at least three tokens into
 // its sequence, so the window rolls over the packed stream across sequence
@@ -147,27 +172,15 @@ __device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int
     for (int k = 0; k < kPass; ++k) cur[k] = buffer_load<kStream>(xbuf, xoff(q0 + k));
 
     // the sequence holding q0: its first token a, its end e, and its routing
-    int i = find_seq(p.starts, p.n, q0, lane), a = 0, e = 0;
-    bool ok = false, live = false;
-    auto enter = [&](int next) {
-        i = next;
-        ok = i >= 0 && i < p.n;
-        if (ok) {
-            a = load_uniform(p.starts, i);
-            e = load_uniform(p.starts, i + 1);
-            ok = a >= 0 && a <= e && e <= p.t;
-            if (!ok && p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
-        }
-        live = ok && route_row(p.idx, p.status, p.n, p.s, i, lane) >= 0;
-    };
-    enter(i);
+    SeqCursor sc;
+    sc.enter(p, find_seq(p.starts, p.n, q0, lane), lane);
     for (int qq = q0; qq < q1; qq += kPass) {
         u32x4 nxt[kPass];
 #pragma unroll
         for (int k = 0; k < kPass; ++k) nxt[k] = buffer_load<kStream>(xbuf, xoff(qq + kPass + k));
         u32x4 ov[kPass];
         uint32_t off[kPass];
-        if (ok && qq - a >= 3 && qq + kPass <= e && qq + kPass <= q1) {
+        if (sc.ok && qq - sc.a >= 3 && qq + kPass <= sc.e && qq + kPass <= q1) {
             // the common pass: inside one sequence, past its first three tokens
 #pragma unroll
             for (int k = 0; k < kPass; ++k) {
@@ -175,7 +188,7 @@ __device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int
                 h0 = h1;
                 h1 = h2;
                 h2 = cur[k];
-                ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};
+                ov[k] = sc.live ? y : u32x4{0u, 0u, 0u, 0u};
                 off[k] = o_tok * (uint32_t)(qq + k - q0) + lane_off;
             }
         } else {
@@ -186,9 +199,9 @@ __device__ __forceinline__ void chunk_packed(const PrefillParams &p, int q0, int
                 h0 = h1;
                 h1 = h2;
                 h2 = cur[k];
-                while (ok && q < q1 && q >= e) enter(i + 1);  // past the end of this (or an empty) sequence
-                ov[k] = live ? y : u32x4{0u, 0u, 0u, 0u};
-                off[k] = ((ok && q < q1 && q - a >= 3) ? o_tok * (uint32_t)(q - q0) : kBadToken) + lane_off;
+                if (q < q1) sc.advance(p, q, lane);
+                ov[k] = sc.live ? y : u32x4{0u, 0u, 0u, 0u};
+                off[k] = ((sc.ok && q < q1 && q - sc.a >= 3) ? o_tok * (uint32_t)(q - q0) : kBadToken) + lane_off;
             }
         }
 #pragma unroll
@@ -240,11 +253,148 @@ __device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weigh
     }
 }
 
-// One block of the edge role: block unit bu = (pair of sequences, tile).
+// ---- the sweep role ---------------------------------------------------------
+// Tokens per wave and waves per block of the sweep role; an item is kSweepSpan
+// consecutive tokens of one 512-channel tile.
+constexpr int kSweepG = 8;
+constexpr int kSweepWaves = 4;
+constexpr int kSweepSpan = kSweepG * kSweepWaves;
+constexpr int kSweepBlock = kWave * kSweepWaves;
+
+// This lane's 8 channels x 4 taps (64 contiguous bytes of the [D, 4] weight) as
+// FP32, channel-major; zeros for a lane past a ragged tile.
+__device__ __forceinline__ void lane_weights(const uint16_t *weight, int c0, uint32_t vec_bytes, uint32_t lane_bytes,
+                                             float (&wf)[32]) {
+    const Buffer wbuf = make_buffer(weight + (int64_t)c0 * 4, vec_bytes * 4u);
+    u32x4 wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wd[k] = buffer_load<kCached>(wbuf, lane_bytes * 4u + 16u * (uint32_t)k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wf[8 * k + 2 * q] = lo_f32(wd[k][q]);
+            wf[8 * k + 2 * q + 1] = hi_f32(wd[k][q]);
+        }
+}
+
+// One block of the sweep role, block b of `grid` (a multiple of tiles, so the
+// block keeps one tile and its weights): items b, b + grid, ... in memory order,
+// item = (group of kSweepSpan tokens, tile) with the tile fastest.  Wave w
+// takes tokens [g0 + w*kSweepG, +kSweepG) of the item's [g0, g1); wave 0 loads
+// the 3 tokens before g0, every other wave takes its 3 from the previous wave's
+// last three through LDS (`tails`, kSweepWaves x 3 vectors per lane).  The
+// batch form's groups do not cross sequences; the packed form's run over the
+// packed stream, and the sequence table decides the stores as in chunk_packed.
+template <int ACT, bool HAS_BIAS>
+__device__ __forceinline__ void sweep_block(const PrefillParams &p, u32x4 *tails, int tiles, int64_t items,
+                                            int64_t groups_per_seq, int64_t b, int64_t grid) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane_bytes = (uint32_t)lane * 16u;
+    const int tile = (int)(b % tiles);
+    const int c0 = tile * kChPerWave;
+    const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
+    const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
+    const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
+    const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u;
+    const bool packed = p.starts != nullptr;
+    float wf[32], bf[8];
+    {
+        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+        if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
+        lane_weights(p.weight, c0, vec_bytes, lane_bytes, wf);
+        unpack_bias(bv, bf);
+    }
+    for (int64_t item = b; item < items; item += grid) {  // block-uniform
+        const int64_t group = item / tiles;
+        const int i = packed ? 0 : (int)(group / groups_per_seq);
+        const int g0 = (int)(packed ? group : group % groups_per_seq) * kSweepSpan;
+        const int g1 = min(p.t, g0 + kSweepSpan);
+        const int lo = max(g0 - 3, 0);
+        const int j0 = g0 + wave * kSweepG;
+        const uint16_t *xs = p.x + (packed ? 0 : (int64_t)i * p.xs_n) + c0;
+        uint16_t *os = p.out + (packed ? 0 : (int64_t)i * p.os_n) + c0;
+        const Buffer xbuf = make_buffer(xs + (int64_t)lo * p.xs_t, x_tok * (uint32_t)(g1 - 1 - lo) + vec_bytes);
+        const Buffer obuf = make_buffer(os + (int64_t)g0 * p.os_t, o_tok * (uint32_t)(g1 - 1 - g0) + vec_bytes);
+        auto xoff = [&](int j) -> uint32_t {
+            return ((j >= lo && j < g1) ? x_tok * (uint32_t)(j - lo) : kBadToken) + lane_off;
+        };
+        // v[k] holds token j0 - 3 + k
+        u32x4 v[kSweepG + 3];
+#pragma unroll
+        for (int k = 0; k < kSweepG; ++k) v[k + 3] = buffer_load<kStream>(xbuf, xoff(j0 + k));
+        if (wave == 0) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) v[k] = buffer_load<kStream>(xbuf, xoff(g0 - 3 + k));
+        }
+
+        // which of this wave's outputs are stored (the edge role writes each
+        // sequence's first three), and which are zeros (padding, rejected)
+        uint32_t off[kSweepG];
+        bool live[kSweepG];
+        if (!packed) {
+            const bool row_live = route_row(p.idx, p.status, p.n, p.s, i, lane) >= 0;
+#pragma unroll
+            for (int k = 0; k < kSweepG; ++k) {
+                const int j = j0 + k;
+                off[k] = ((j >= 3 && j < g1) ? o_tok * (uint32_t)(j - g0) : kBadToken) + lane_off;
+                live[k] = row_live;
+            }
+        } else if (j0 < g1) {
+            SeqCursor sc;
+            sc.enter(p, find_seq(p.starts, p.n, j0, lane), lane);
+            if (sc.ok && j0 - sc.a >= 3 && j0 + kSweepG <= sc.e && j0 + kSweepG <= g1) {
+#pragma unroll
+                for (int k = 0; k < kSweepG; ++k) {
+                    off[k] = o_tok * (uint32_t)(j0 + k - g0) + lane_off;
+                    live[k] = sc.live;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kSweepG; ++k) {
+                    const int q = j0 + k;
+                    if (q < g1) sc.advance(p, q, lane);
+                    off[k] = ((sc.ok && q < g1 && q - sc.a >= 3) ? o_tok * (uint32_t)(q - g0) : kBadToken) + lane_off;
+                    live[k] = sc.live;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kSweepG; ++k) {
+                off[k] = kBadToken + lane_off;
+                live[k] = false;
+            }
+        }
+
+        // the halos: publish this wave's last three tokens, take the previous wave's
+        u32x4 *mine = tails + wave * 3 * kWave;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) mine[k * kWave + lane] = v[kSweepG + k];
+        __syncthreads();
+        if (wave > 0) {
+            const u32x4 *prev = tails + (wave - 1) * 3 * kWave;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) v[k] = prev[k * kWave + lane];
+        }
+        // outputs from the last, each in place of its own token
+#pragma unroll
+        for (int k = kSweepG - 1; k >= 0; --k) {
+            const u32x4 y = conv8<ACT>(v[k], v[k + 1], v[k + 2], v[k + 3], wf, bf);
+            v[k + 3] = live[k] ? y : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < kSweepG; ++k) buffer_store<kStream>(v[k + 3], obuf, off[k]);
+        __syncthreads();  // the tails are rewritten by the next item
+    }
+}
+
+// One block of the edge role: block unit bu = (WPB sequences, tile).
 // stage_all holds kWave * L vectors per wave: the compact state's
 // transposition, then the planes, which the final state picks at a run-time
-// position.
-template <int L, int ACT, int LAYOUT>
+// position.  Two-wave blocks share the tile's weights through weight_tile;
+// other blocks load each lane's weights directly.
+template <int L, int ACT, int LAYOUT, int WPB>
 __device__ __forceinline__ void edge_block(const PrefillParams &p, u32x4 *stage_all, u32x4 *weight_tile, int tiles,
                                            int64_t bu) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -253,7 +403,7 @@ __device__ __forceinline__ void edge_block(const PrefillParams &p, u32x4 *stage_
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
     {
         const int tile = (int)(bu % tiles);
-        const int i_raw = (int)(bu / tiles) * kWavesPerBlock + wave;
+        const int i_raw = (int)(bu / tiles) * WPB + wave;
         const int c0 = tile * kChPerWave;
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
@@ -284,7 +434,7 @@ __device__ __forceinline__ void edge_block(const PrefillParams &p, u32x4 *stage_
 
         __builtin_amdgcn_s_setprio(3);
         u32x4 wraw[kWeightChunks];
-        weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
+        if constexpr (WPB == kWavesPerBlock) weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         const u32x4 bv = buffer_load<kCached>(make_buffer(p.bias != nullptr ? p.bias + c0 : p.weight,
                                                           p.bias != nullptr ? vec_bytes : 0u),
                                               lane_bytes);
@@ -321,7 +471,10 @@ __device__ __forceinline__ void edge_block(const PrefillParams &p, u32x4 *stage_
         __builtin_amdgcn_s_setprio(0);
 
         float wf[32], bf[8];
-        weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        if constexpr (WPB == kWavesPerBlock)
+            weight_tile_share(weight_tile, wraw, wave, lane, wf);
+        else
+            lane_weights(p.weight, c0, vec_bytes, lane_bytes, wf);
         unpack_bias(bv, bf);
 
         u32x4 pl[L];
@@ -408,10 +561,24 @@ __global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles,
     const int64_t total = edge_blocks + chunk_blocks;
     for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
         if (b < edge_blocks)
-            edge_block<L, ACT, LAYOUT>(p, stage_all, weight_tile, tiles, b);
+            edge_block<L, ACT, LAYOUT, kWavesPerBlock>(p, stage_all, weight_tile, tiles, b);
         else
             chunk_block<ACT, HAS_BIAS>(p, weight_tile, tiles, chunk, units, units_per_seq, b - edge_blocks);
     }
+}
+
+// The sweep form of the same call: `grid` sweep blocks (all resident at once),
+// then the edge role in blocks of kSweepWaves sequences, which start as the
+// first sweep blocks finish.
+template <int L, int ACT, int LAYOUT, bool HAS_BIAS>
+__global__ __launch_bounds__(kSweepBlock) void prefill_sweep_v8(PrefillParams p, int tiles, int64_t items,
+                                                                int64_t groups_per_seq, int64_t grid) {
+    __shared__ u32x4 lds[kSweepWaves * kWave * L];  // the sweep role's halos, or the edge role's stages
+    const int64_t b = blockIdx.x;
+    if (b < grid)
+        sweep_block<ACT, HAS_BIAS>(p, lds, tiles, items, groups_per_seq, b, grid);
+    else
+        edge_block<L, ACT, LAYOUT, kSweepWaves>(p, lds, nullptr, tiles, b - grid);
 }
 
 template <int ACT>
@@ -486,19 +653,64 @@ hipError_t launch(Kernel kernel, int64_t blocks, int block, hipStream_t stream, 
                            stream);
 }
 
+// Blocks of `kernel` (at `block` threads) that the GPU holds at once, or 0.
+int resident_blocks(const void *kernel, int block) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+// The sweep grid: a multiple of `tiles` within [cap / 2, cap] (cap = the blocks
+// resident at once) that pads `items` least, the larger on a tie; every block
+// then does ceil(items / grid) or one fewer items.
+int64_t sweep_grid(int64_t items, int tiles, int64_t cap) {
+    const int64_t gmax = cap / tiles * tiles;
+    if (gmax < tiles) return 0;
+    if (items <= gmax) return items;
+    int64_t best = gmax, best_cost = (items + gmax - 1) / gmax * gmax;
+    for (int64_t g = gmax - tiles; g >= gmax / 2 && g >= tiles; g -= tiles) {
+        const int64_t cost = (items + g - 1) / g * g;
+        if (cost < best_cost) {
+            best = g;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+// Column (chunk) or sweep form.  A/B on MI355X: the sweep wins where rows are
+// narrow (D <= 4096: 7-25 %) or the columns short (64-token chunks at D = 8192:
+// 6 %); long columns of wide rows run 1-3 % faster as chunks.
 template <int L, int ACT, int LAYOUT>
-hipError_t launch_prefill_l(const PrefillParams &p, int tiles, hipStream_t stream) {
-    const int64_t tokens = p.starts != nullptr ? (int64_t)p.t : (int64_t)p.t * p.n;
+hipError_t launch_prefill_l(const PrefillParams &p, int tiles, hipStream_t stream, bool *swept) {
+    const bool packed = p.starts != nullptr;
+    const int64_t tokens = packed ? (int64_t)p.t : (int64_t)p.t * p.n;
     int64_t chunk = (tokens * tiles + kTargetWaves - 1) / kTargetWaves;
     chunk = (chunk + kPass - 1) / kPass * kPass;
     chunk = chunk < kMinChunk ? kMinChunk : chunk > kMaxChunk ? kMaxChunk : chunk;
+    PrefillParams pp = p;
+    *swept = false;
+    if (p.d <= 4096 || chunk <= 64) {
+        const int64_t groups_per_seq = ((int64_t)p.t + kSweepSpan - 1) / kSweepSpan;
+        const int64_t items = (packed ? groups_per_seq : groups_per_seq * p.n) * tiles;
+        const int64_t edge_blocks = ((int64_t)p.n + kSweepWaves - 1) / kSweepWaves * tiles;
+        auto kernel = p.bias != nullptr ? prefill_sweep_v8<L, ACT, LAYOUT, true> : prefill_sweep_v8<L, ACT, LAYOUT, false>;
+        static const int resident = resident_blocks(reinterpret_cast<const void *>(kernel), kSweepBlock);
+        const int64_t grid = sweep_grid(items, tiles, resident);
+        if (grid > 0 && grid + edge_blocks < kMaxBlocks) {
+            *swept = true;
+            return launch(kernel, grid + edge_blocks, kSweepBlock, stream, pp, tiles, items, groups_per_seq, grid);
+        }
+    }
     const int64_t units_per_seq = ((int64_t)p.t + chunk - 1) / chunk;
-    const int64_t units = p.starts != nullptr ? units_per_seq : units_per_seq * p.n;
+    const int64_t units = packed ? units_per_seq : units_per_seq * p.n;
     const int64_t chunk_blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
     const int64_t edge_blocks = ((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock * tiles;
     const int64_t total = edge_blocks + chunk_blocks;
     const int64_t grid = total < kMaxBlocks ? total : kMaxBlocks;
-    PrefillParams pp = p;
     const int ch = (int)chunk;
     return p.bias != nullptr
                ? launch(prefill_v8<L, ACT, LAYOUT, true>, grid, kBlock, stream, pp, tiles, ch, units, units_per_seq,
@@ -509,20 +721,21 @@ hipError_t launch_prefill_l(const PrefillParams &p, int tiles, hipStream_t strea
 
 template <int ACT, int LAYOUT>
 hipError_t launch_prefill_layout(const PrefillParams &p, int tiles, hipStream_t stream, const char **name) {
-#define DCCONV_PF_NAME(LL)                                                                              \
-    (LAYOUT == kStateless                                                                               \
-         ? (ACT ? "prefill_v8<stateless,silu>" : "prefill_v8<stateless,identity>")                      \
-         : LAYOUT == kCompactState                                                                      \
-               ? (ACT ? "prefill_v8<L=" #LL ",silu,compact>" : "prefill_v8<L=" #LL ",identity,compact>") \
-               : (ACT ? "prefill_v8<L=" #LL ",silu,channel_last>"                                       \
-                      : "prefill_v8<L=" #LL ",identity,channel_last>"))
-#define DCCONV_PF_CASE(LL)          \
-    case LL:                        \
-        *name = DCCONV_PF_NAME(LL); \
-        return launch_prefill_l<LL, ACT, LAYOUT>(p, tiles, stream);
+#define DCCONV_PF_NAME(KN, LL)                                                            \
+    (LAYOUT == kStateless                                                                 \
+         ? (ACT ? KN "<stateless,silu>" : KN "<stateless,identity>")                      \
+         : LAYOUT == kCompactState                                                        \
+               ? (ACT ? KN "<L=" #LL ",silu,compact>" : KN "<L=" #LL ",identity,compact>") \
+               : (ACT ? KN "<L=" #LL ",silu,channel_last>" : KN "<L=" #LL ",identity,channel_last>"))
+#define DCCONV_PF_CASE(LL)                                                                             \
+    case LL: {                                                                                         \
+        bool swept = false;                                                                            \
+        const hipError_t err = launch_prefill_l<LL, ACT, LAYOUT>(p, tiles, stream, &swept);            \
+        *name = swept ? DCCONV_PF_NAME("prefill_sweep_v8", LL) : DCCONV_PF_NAME("prefill_v8", LL);     \
+        return err;                                                                                    \
+    }
     if constexpr (LAYOUT == kStateless) {
-        *name = DCCONV_PF_NAME(3);
-        return launch_prefill_l<3, ACT, kStateless>(p, tiles, stream);
+        switch (3) { DCCONV_PF_CASE(3) }
     } else {
         switch (p.l) {
             DCCONV_PF_CASE(3)
@@ -536,6 +749,7 @@ hipError_t launch_prefill_layout(const PrefillParams &p, int tiles, hipStream_t 
     }
 #undef DCCONV_PF_CASE
 #undef DCCONV_PF_NAME
+    return hipErrorInvalidValue;
 }
 
 template <int ACT>

@@ -137,7 +137,7 @@ def test_prefill_batch_compact(L, T):
     case = PrefillCase(2000 + 10 * L + T, 1096, N=3, T=T, L=L, state="compact", bias=T % 2 == 0,
                        act=None if T % 3 == 0 else "silu")
     case.check()
-    assert case.kernel == f"prefill_v8<L={L},{'identity' if T % 3 == 0 else 'silu'},compact>", case.kernel
+    assert case.kernel == f"prefill_sweep_v8<L={L},{'identity' if T % 3 == 0 else 'silu'},compact>", case.kernel
 
 
 @pytest.mark.parametrize("L", [3, 5, 6, 7, 8])
@@ -153,7 +153,48 @@ def test_prefill_batch_channel_last(L, T):
 def test_prefill_stateless(T):
     case = PrefillCase(2200 + T, 520, N=4, T=T, state=None, bias=True)
     case.check()
-    assert case.kernel == "prefill_v8<stateless,silu>", case.kernel
+    assert case.kernel == "prefill_sweep_v8<stateless,silu>", case.kernel
+
+
+# Which form a call takes: the sweep for rows of at most 4096 channels or
+# columns of at most 64 tokens, the chunk (column) form otherwise.  D = 4616 has
+# a ragged last tile of one lane.
+
+@pytest.mark.parametrize("layout", ["compact", "channel_last", None])
+def test_prefill_column_form(layout):
+    case = PrefillCase(2250, 4616, N=8, T=1700, L=4 if layout == "compact" else 3, state=layout,
+                       routing="padded" if layout else "none", n_pad=2, S=10, bias=True, has_init="mixed",
+                       status=layout is not None)
+    assert case.check() in (None, 0)
+    assert case.kernel.startswith("prefill_v8<"), case.kernel
+
+
+def test_prefill_column_form_packed():
+    rng = np.random.default_rng(2260)
+    lens = [int(v) for v in rng.integers(1500, 3000, size=9)] + [0, 2]
+    case = PrefillCase(2260, 4616, lens=lens, L=5, state="compact", routing="unique", S=12, has_init="mixed",
+                       status=True)
+    assert case.check() == 0
+    assert case.kernel.startswith("prefill_v8<L=5,"), case.kernel
+
+
+@pytest.mark.parametrize("layout", ["compact", "channel_last"])
+def test_prefill_sweep_form_wide_short(layout):
+    """Wide rows but short columns (64 tokens or fewer per chunk wave) take the sweep."""
+    case = PrefillCase(2270, 8192, N=2, T=300, L=3, state=layout, has_init="all", bias=True)
+    case.check()
+    assert case.kernel.startswith("prefill_sweep_v8<L=3,"), case.kernel
+
+
+def test_prefill_sweep_packed_many_short_sequences():
+    """Packed sequences shorter than a sweep item (32 tokens): items span many
+    sequences, and a wave's 8 tokens cross several boundaries."""
+    rng = np.random.default_rng(2280)
+    lens = [int(v) for v in rng.integers(0, 12, size=700)]
+    case = PrefillCase(2280, 1032, lens=lens, L=3, state="channel_last", routing="padded", n_pad=40, S=700,
+                       has_init="mixed", status=True, bias=True)
+    assert case.check() == 0
+    assert case.kernel.startswith("prefill_sweep_v8<"), case.kernel
 
 
 def test_prefill_zero_tokens_writes_final_states():
