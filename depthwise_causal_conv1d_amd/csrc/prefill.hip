@@ -8,8 +8,10 @@
 //   out[i, c, j] = act(sum_k ext[L + j - 3 + k] * w[c, k] + bias[c])
 //   final state  = ext[T : T + L]
 //
-// Outputs j >= 3 depend on x alone, so they need no ordering at all.  One
-// kernel, prefill_v8<L, ACT, layout, HAS_BIAS>, has two kinds of blocks:
+// Outputs j >= 3 depend on x alone, so they need no ordering at all.  A call
+// is one launch of one of two kernels, each with two roles: the edge role and
+// a streaming role for the rest.  prefill_v8<L, ACT, layout, HAS_BIAS> (the
+// column form, for wide rows with long columns):
 //  * chunk blocks: one wavefront per (512-channel tile,
 //    chunk of tokens), 8 channels per lane; the block's two waves take
 //    neighbouring chunks of one tile and share its weights.  The chunk length
@@ -24,10 +26,17 @@
 //    replaces it -- one wavefront per (sequence, tile), so each slot is read
 //    and written by exactly one wave.  They come first in the grid, so their
 //    short dependent chains run under the chunk blocks' streaming.
-//  * prefill_scalar<ACT>: one thread per (sequence, channel) walking its
-//    tokens in order; any strides, any L >= 3.
-// The two roles write disjoint outputs and read x only, so they need no
-// ordering between them.
+// prefill_sweep_v8<L, ACT, layout, HAS_BIAS> (the sweep form, for rows of at
+// most 4096 channels or columns of at most 64 tokens): blocks of four waves,
+// as many as the GPU holds at once, walk (32-token group, tile) items in
+// memory order, so every block does nearly the same work and the grid reads
+// one compact stretch of x at a time; a group's halo comes from the previous
+// wave through LDS (see sweep_block).  Its edge blocks come after the sweep
+// blocks and start as the first of those finish.  prefill_scalar<ACT> serves
+// everything else (any strides, any L >= 3): one thread per (sequence,
+// channel) walking its tokens in order.
+// The roles write disjoint outputs and read x only, so they need no ordering
+// between them.
 #include <stdint.h>
 
 #include "dcconv.h"
