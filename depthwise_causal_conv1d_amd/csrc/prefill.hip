@@ -576,18 +576,21 @@ __global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles,
     }
 }
 
-// The sweep form of the same call: `grid` sweep blocks (all resident at once),
-// then the edge role in blocks of kSweepWaves sequences, which start as the
-// first sweep blocks finish.
+// The sweep form of the same call: `grid` sweep blocks and `edge_blocks` edge
+// blocks of kSweepWaves sequences.  With few edge blocks they come last and
+// start as the first sweep blocks finish; with many (many short sequences) they
+// come first and the sweep grid leaves room for them.
 template <int L, int ACT, int LAYOUT, bool HAS_BIAS>
 __global__ __launch_bounds__(kSweepBlock) void prefill_sweep_v8(PrefillParams p, int tiles, int64_t items,
-                                                                int64_t groups_per_seq, int64_t grid) {
+                                                                int64_t groups_per_seq, int64_t grid,
+                                                                int64_t edge_blocks, int edges_first) {
     __shared__ u32x4 lds[kSweepWaves * kWave * L];  // the sweep role's halos, or the edge role's stages
     const int64_t b = blockIdx.x;
-    if (b < grid)
-        sweep_block<ACT, HAS_BIAS>(p, lds, tiles, items, groups_per_seq, b, grid);
+    const int64_t sweep_b = edges_first ? b - edge_blocks : b;
+    if (sweep_b >= 0 && sweep_b < grid)
+        sweep_block<ACT, HAS_BIAS>(p, lds, tiles, items, groups_per_seq, sweep_b, grid);
     else
-        edge_block<L, ACT, LAYOUT, kSweepWaves>(p, lds, nullptr, tiles, b - grid);
+        edge_block<L, ACT, LAYOUT, kSweepWaves>(p, lds, nullptr, tiles, edges_first ? b : b - grid);
 }
 
 template <int ACT>
@@ -662,14 +665,22 @@ hipError_t launch(Kernel kernel, int64_t blocks, int block, hipStream_t stream, 
                            stream);
 }
 
-// Blocks of `kernel` (at `block` threads) that the GPU holds at once, or 0.
-int resident_blocks(const void *kernel, int block) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+// Blocks of `kernel` (at `block` threads) that the current device holds at
+// once, or 0.  `cache` holds the answer per device (a partitioned GPU shows
+// devices of different sizes); concurrent first calls store the same value.
+constexpr int kMaxDevices = 64;
+int resident_blocks(const void *kernel, int block, int (&cache)[kMaxDevices]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices && __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) > 0)
+        return __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
         return 0;
-    return cus * per_cu;
+    const int n = cus * per_cu;
+    if (dev < kMaxDevices) __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    return n;
 }
 
 // The sweep grid: a multiple of `tiles` within [cap / 2, cap] (cap = the blocks
@@ -707,11 +718,16 @@ hipError_t launch_prefill_l(const PrefillParams &p, int tiles, hipStream_t strea
         const int64_t items = (packed ? groups_per_seq : groups_per_seq * p.n) * tiles;
         const int64_t edge_blocks = ((int64_t)p.n + kSweepWaves - 1) / kSweepWaves * tiles;
         auto kernel = p.bias != nullptr ? prefill_sweep_v8<L, ACT, LAYOUT, true> : prefill_sweep_v8<L, ACT, LAYOUT, false>;
-        static const int resident = resident_blocks(reinterpret_cast<const void *>(kernel), kSweepBlock);
-        const int64_t grid = sweep_grid(items, tiles, resident);
+        static int cache[kMaxDevices];
+        const int64_t resident = resident_blocks(reinterpret_cast<const void *>(kernel), kSweepBlock, cache);
+        const int edges_first = edge_blocks > resident / 8;
+        const int64_t cap = edges_first ? (resident - edge_blocks > resident / 2 ? resident - edge_blocks : resident / 2)
+                                        : resident;
+        const int64_t grid = sweep_grid(items, tiles, cap);
         if (grid > 0 && grid + edge_blocks < kMaxBlocks) {
             *swept = true;
-            return launch(kernel, grid + edge_blocks, kSweepBlock, stream, pp, tiles, items, groups_per_seq, grid);
+            return launch(kernel, grid + edge_blocks, kSweepBlock, stream, pp, tiles, items, groups_per_seq, grid,
+                          edge_blocks, edges_first);
         }
     }
     const int64_t units_per_seq = ((int64_t)p.t + chunk - 1) / chunk;
