@@ -9,7 +9,7 @@
 // once instead of T times: per active channel-row the bytes drop from
 // T * (4 + 4L) + 2T to 4L + 4T (compact layout).
 //
-//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP, SPLIT>: one wavefront owns
+//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP, SPLIT, PREFETCH>: one wavefront owns
 //    R rows of one 512-channel tile (8 channels per lane), the block shares the
 //    tile's weights.  With SPLIT (one row per block, T >= 2L) the block's two
 //    waves share one row and split its tokens at h = T/2: outputs from token 3
@@ -21,10 +21,12 @@
 //    The history lives in registers in plane-major form (one 16-byte vector per
 //    history position, 8 channels each), so a token's shift is a renaming of
 //    registers.  Tokens go in passes of KP: the pass's x vectors are all loaded
-//    before the first is used (with one row per wave, the next pass's loads
-//    are issued before this pass is computed) and its outputs are all stored
-//    after the last is computed.  Compact state goes through the same LDS stage as the
-//    single-token kernel; channel-last state is already plane-major.
+//    before the first is used (with PREFETCH, for one-row waves of several
+//    passes, the next pass's loads are issued before this pass is computed)
+//    and its outputs are all stored after the last is computed.  A one-row
+//    wave of 5 to 8 tokens takes them in a single pass of 8.  Compact state
+//    goes through the same LDS stage as the single-token kernel; channel-last
+//    state is already plane-major.
 //  * tokens_scalar<ACT>: one thread per (row, channel), any strides, any L >= 3;
 //    each token is one single-step update of the thread's channel in memory.
 #include <stdint.h>
@@ -42,9 +44,10 @@ namespace {
 constexpr uint32_t kBadToken = 1u << 30;
 constexpr uint32_t kBadLane = 1u << 31;
 
-template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP, bool SPLIT>
+template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP, bool SPLIT, bool PREFETCH>
 __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_per_row, int64_t block_units) {
     static_assert(!SPLIT || R == 1, "a split block holds one row");
+    static_assert(!PREFETCH || R == 1, "only one-row waves prefetch");
     __shared__ u32x4 stage_all[kWavesPerBlock][CHANNEL_LAST ? 1 : kWave * L];
     __shared__ u32x4 weight_tile[4 * kWave];
     // Positions read in the channel-last layout: the first token's taps need
@@ -178,11 +181,13 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
             __syncthreads();
         }
 
-        // One row per wave: the next pass's x is loaded before this pass is
-        // computed, so its latency runs under this pass's arithmetic and stores
-        // (a thin grid has no other wave on the SIMD to cover it).  Two rows
-        // per wave load each pass at its start and keep the registers.
-        constexpr bool kPrefetch = R == 1;
+        // PREFETCH (one row per wave, more than one pass): the next pass's x
+        // is loaded before this pass is computed, so its latency runs under
+        // this pass's arithmetic and stores (a thin grid has no other wave on
+        // the SIMD to cover it).  Otherwise each pass is loaded at its start;
+        // a wave whose tokens fit one pass then has every load issued before
+        // its first store, so its waits never cover a store.
+        constexpr bool kPrefetch = PREFETCH;
         for (int t0 = tb; t0 < te; t0 += KP) {
             u32x4 xn[R][KP];
             if (kPrefetch && t0 + KP < te) {  // wave-uniform
@@ -308,13 +313,15 @@ hipError_t launch_tokens(Kernel kernel, const TokensParams &p, int tiles_per_row
                            stream);
 }
 
-template <int L, int ACT, bool CL, int R, int KP, bool SPLIT = false>
+template <int L, int ACT, bool CL, int R, int KP, bool SPLIT, bool PREFETCH>
 hipError_t launch_tokens_l(const TokensParams &p, int tiles, hipStream_t stream) {
     const int64_t rows_per_block = SPLIT ? 1 : kWavesPerBlock * R;
     const int64_t block_units = tiles * (((int64_t)p.n + rows_per_block - 1) / rows_per_block);
     return p.bias != nullptr
-               ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP, SPLIT>, p, tiles, block_units, kBlock, stream)
-               : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP, SPLIT>, p, tiles, block_units, kBlock, stream);
+               ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP, SPLIT, PREFETCH>, p, tiles, block_units, kBlock,
+                               stream)
+               : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP, SPLIT, PREFETCH>, p, tiles, block_units, kBlock,
+                               stream);
 }
 
 // A grid of one row per wave below this many waves (under two per SIMD) splits
@@ -325,29 +332,40 @@ template <int ACT, bool CL>
 hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream, const char **name) {
     // Two rows per wave when the history is short and the grid still fills the
     // chip with them; else one row per wave, its tokens split over two waves
-    // when the grid is thin and the call long.  Passes of 4 tokens (with the
-    // next pass in flight) keep every form within 256 registers.
+    // when the grid is thin and the call long.  A one-row wave with 5 to 8
+    // tokens takes them in one pass of 8; longer ones go in passes of 4 with
+    // the next pass in flight.  Every form stays within 256 registers.
     const bool two = p.l <= 4 && ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
     const bool split = !two && (int64_t)p.n * tiles < kMaxWavesForSplit && p.t >= 2 * p.l;
+    const int per_wave = split ? p.t - p.t / 2 : p.t;
+    const bool one_pass = per_wave > 4 && per_wave <= 8;
 #define DCCONV_TOK_NAME(LL, SUF)                                                              \
     (CL ? (ACT ? "tokens_v8<L=" #LL ",silu,channel_last," SUF ">"                            \
                : "tokens_v8<L=" #LL ",identity,channel_last," SUF ">")                       \
         : (ACT ? "tokens_v8<L=" #LL ",silu,compact," SUF ">" : "tokens_v8<L=" #LL ",identity,compact," SUF ">"))
-#define DCCONV_TOK_CASE(LL)                                                    \
-    case LL:                                                                   \
-        if (split) {                                                           \
-            *name = DCCONV_TOK_NAME(LL, "R=1,split");                          \
-            return launch_tokens_l<LL, ACT, CL, 1, 4, true>(p, tiles, stream); \
-        }                                                                      \
-        *name = DCCONV_TOK_NAME(LL, "R=1");                                    \
-        return launch_tokens_l<LL, ACT, CL, 1, 4>(p, tiles, stream);
+#define DCCONV_TOK_CASE(LL)                                                                   \
+    case LL:                                                                                  \
+        if (split && one_pass) {                                                              \
+            *name = DCCONV_TOK_NAME(LL, "R=1,split,one pass");                                \
+            return launch_tokens_l<LL, ACT, CL, 1, 8, true, false>(p, tiles, stream);         \
+        }                                                                                     \
+        if (split) {                                                                          \
+            *name = DCCONV_TOK_NAME(LL, "R=1,split");                                         \
+            return launch_tokens_l<LL, ACT, CL, 1, 4, true, true>(p, tiles, stream);          \
+        }                                                                                     \
+        if (one_pass) {                                                                       \
+            *name = DCCONV_TOK_NAME(LL, "R=1,one pass");                                      \
+            return launch_tokens_l<LL, ACT, CL, 1, 8, false, false>(p, tiles, stream);        \
+        }                                                                                     \
+        *name = DCCONV_TOK_NAME(LL, "R=1");                                                   \
+        return launch_tokens_l<LL, ACT, CL, 1, 4, false, true>(p, tiles, stream);
     if (two) {
         if (p.l == 3) {
             *name = DCCONV_TOK_NAME(3, "R=2");
-            return launch_tokens_l<3, ACT, CL, 2, 4>(p, tiles, stream);
+            return launch_tokens_l<3, ACT, CL, 2, 4, false, false>(p, tiles, stream);
         }
         *name = DCCONV_TOK_NAME(4, "R=2");
-        return launch_tokens_l<4, ACT, CL, 2, 4>(p, tiles, stream);
+        return launch_tokens_l<4, ACT, CL, 2, 4, false, false>(p, tiles, stream);
     }
     switch (p.l) {
         DCCONV_TOK_CASE(3)

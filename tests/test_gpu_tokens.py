@@ -123,8 +123,11 @@ class TokensCase:
 
 def _one_row_form(T, L):
     """Kernel-name suffix of the one-row form on a thin grid: a call of at least
-    2L tokens splits each row's tokens over two waves."""
-    return "R=1,split>" if T >= 2 * L else "R=1>"
+    2L tokens splits each row's tokens over two waves, and a wave with 5 to 8
+    tokens takes them in one pass."""
+    split = T >= 2 * L
+    per_wave = T - T // 2 if split else T
+    return "R=1" + (",split" if split else "") + (",one pass" if 4 < per_wave <= 8 else "") + ">"
 
 
 @pytest.mark.parametrize("L", [3, 4, 8])
@@ -174,7 +177,7 @@ def test_tokens_long_history_in_one_call():
     case.indices = case.oracle_indices = data["indices"]
     case.act, case.layout, case.out_layout, case.status = spec.act, spec.layout, "token_major", True
     assert case.check() == 0
-    assert case.kernel == "tokens_v8<L=8,identity,compact,R=1,split>", case.kernel
+    assert case.kernel == "tokens_v8<L=8,identity,compact,R=1,split,one pass>", case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
@@ -207,7 +210,8 @@ def test_tokens_split_rows(layout, L, T):
     case = TokensCase(2300 + 10 * L + T, N=10, D=1096, T=T, L=L, layout=layout, bias=True, routing="padded",
                       n_pad=3, S=14, status=True, act="silu" if T % 2 else None)
     assert case.check() == 0
-    assert case.kernel == f"tokens_v8<L={L},{'silu' if T % 2 else 'identity'},{layout},R=1,split>", case.kernel
+    assert case.kernel == f"tokens_v8<L={L},{'silu' if T % 2 else 'identity'},{layout}," + _one_row_form(T, L), \
+        case.kernel
 
 
 def test_tokens_one_row_full_grid_does_not_split():
