@@ -23,8 +23,8 @@
 //    registers.  Tokens go in passes of KP: the pass's x vectors are all loaded
 //    before the first is used (with PREFETCH, for one-row waves of several
 //    passes, the next pass's loads are issued before this pass is computed)
-//    and its outputs are all stored after the last is computed.  A one-row
-//    wave of 5 to 8 tokens takes them in a single pass of 8.  Compact state
+//    and its outputs are all stored after the last is computed.  A wave of 5
+//    to 8 tokens takes them in a single pass of 8.  Compact state
 //    goes through the same LDS stage as the single-token kernel; channel-last
 //    state is already plane-major.
 //  * tokens_scalar<ACT>: one thread per (row, channel), any strides, any L >= 3;
@@ -332,9 +332,10 @@ template <int ACT, bool CL>
 hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream, const char **name) {
     // Two rows per wave when the history is short and the grid still fills the
     // chip with them; else one row per wave, its tokens split over two waves
-    // when the grid is thin and the call long.  A one-row wave with 5 to 8
-    // tokens takes them in one pass of 8; longer ones go in passes of 4 with
-    // the next pass in flight.  Every form stays within 256 registers.
+    // when the grid is thin and the call long.  A wave with 5 to 8 tokens takes
+    // them in one pass of 8; a longer one-row wave goes in passes of 4 with the
+    // next pass in flight, a longer two-row wave in passes of 4 loaded at their
+    // start.  Every form stays within 256 registers.
     const bool two = p.l <= 4 && ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
     const bool split = !two && (int64_t)p.n * tiles < kMaxWavesForSplit && p.t >= 2 * p.l;
     const int per_wave = split ? p.t - p.t / 2 : p.t;
@@ -360,9 +361,18 @@ hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream
         *name = DCCONV_TOK_NAME(LL, "R=1");                                                   \
         return launch_tokens_l<LL, ACT, CL, 1, 4, false, true>(p, tiles, stream);
     if (two) {
+        const bool one_pass_two = p.t > 4 && p.t <= 8;
         if (p.l == 3) {
+            if (one_pass_two) {
+                *name = DCCONV_TOK_NAME(3, "R=2,one pass");
+                return launch_tokens_l<3, ACT, CL, 2, 8, false, false>(p, tiles, stream);
+            }
             *name = DCCONV_TOK_NAME(3, "R=2");
             return launch_tokens_l<3, ACT, CL, 2, 4, false, false>(p, tiles, stream);
+        }
+        if (one_pass_two) {
+            *name = DCCONV_TOK_NAME(4, "R=2,one pass");
+            return launch_tokens_l<4, ACT, CL, 2, 8, false, false>(p, tiles, stream);
         }
         *name = DCCONV_TOK_NAME(4, "R=2");
         return launch_tokens_l<4, ACT, CL, 2, 4, false, false>(p, tiles, stream);

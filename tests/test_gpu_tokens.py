@@ -180,13 +180,19 @@ def test_tokens_long_history_in_one_call():
     assert case.kernel == "tokens_v8<L=8,identity,compact,R=1,split,one pass>", case.kernel
 
 
+def _two_row_form(T):
+    """Kernel-name suffix of the two-row form: 5 to 8 tokens go in one pass."""
+    return "R=2,one pass>" if 4 < T <= 8 else "R=2>"
+
+
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
-def test_tokens_full_size_large_decode(layout):
-    """The large decode batch (N=256, D=8192, L=3, SiLU) advanced 4 tokens at once,
-    checked element by element against the oracle at full size."""
-    case = TokensCase(1400, N=256, D=8192, T=4, L=3, layout=layout, ldx=8200)
+@pytest.mark.parametrize("T", [4, 8])
+def test_tokens_full_size_large_decode(layout, T):
+    """The large decode batch (N=256, D=8192, L=3, SiLU) advanced 4 or 8 tokens at
+    once, checked element by element against the oracle at full size."""
+    case = TokensCase(1400 + T, N=256, D=8192, T=T, L=3, layout=layout, ldx=8200)
     case.check()
-    assert case.kernel == f"tokens_v8<L=3,silu,{layout},R=2>", case.kernel
+    assert case.kernel == f"tokens_v8<L=3,silu,{layout}," + _two_row_form(T), case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
@@ -197,7 +203,7 @@ def test_tokens_two_rows_per_wave(layout, T):
     case = TokensCase(1450 + T, N=129, D=8192, T=T, L=4, layout=layout, bias=True, routing="padded", n_pad=9,
                       S=160, status=True)
     assert case.check() == 0
-    assert case.kernel == f"tokens_v8<L=4,silu,{layout},R=2>", case.kernel
+    assert case.kernel == f"tokens_v8<L=4,silu,{layout}," + _two_row_form(T), case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
