@@ -392,6 +392,11 @@ hipError_t launch_update_tokens_ring(const TokensParams &p, StateLayout layout, 
     } else {                                   \
         DCCONV_TR_GO(R_, KP_, false, L3_);     \
     }
+        if (two && p.t > 4 && p.t <= 8) {  // one pass of 8: every load before the first store
+            *kernel_name = silu ? "tokens_ring_v8<silu,R=2,one pass>" : "tokens_ring_v8<identity,R=2,one pass>";
+            if (l3) { DCCONV_TR_B(2, 8, true) }
+            DCCONV_TR_B(2, 8, false)
+        }
         if (two) {
             *kernel_name = silu ? "tokens_ring_v8<silu,R=2>" : "tokens_ring_v8<identity,R=2>";
             if (l3) { DCCONV_TR_B(2, 4, true) }
