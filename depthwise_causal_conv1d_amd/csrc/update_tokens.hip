@@ -189,8 +189,11 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
         // its first store, so its waits never cover a store.
         constexpr bool kPrefetch = PREFETCH;
         for (int t0 = tb; t0 < te; t0 += KP) {
+            // The prefetch is issued on the last pass too (its offsets then lie
+            // past the descriptor: nothing is read): with one path into the
+            // pass, each wait covers only the loads it needs.
             u32x4 xn[R][KP];
-            if (kPrefetch && t0 + KP < te) {  // wave-uniform
+            if (kPrefetch) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
                 for (int i = 0; i < KP; ++i)
                     buffer_store<kStream>(ov[r][i], obuf[r],
                                           (t0 + i < te ? o_tok * (uint32_t)(t0 + i) : kBadToken) + lane_off);
-            if (kPrefetch && t0 + KP < te) {
+            if (kPrefetch) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
