@@ -148,7 +148,7 @@ def test_tokens_compact_other_history_lengths(L):
 
 
 @pytest.mark.parametrize("L", [3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("T", [1, 4, 17])
+@pytest.mark.parametrize("T", [1, 4, 7, 17])
 def test_tokens_channel_last(L, T):
     case = TokensCase(1200 + 10 * L + T, N=7, D=1608, T=T, L=L, layout="channel_last", bias=L % 2 == 0,
                       act="silu" if T != 4 else None, routing="unique", S=11)
