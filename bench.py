@@ -452,7 +452,7 @@ def main():
         f"{res['buffer_sets']} buffer sets, wall {res['wall_ms_per_step'] * 1e3:.3f} us/step")
     others = []
     if not args.no_other_workloads:
-        for other in wl.CONFIGS + wl.EXTRA + wl.PREFILL:
+        for other in wl.DECODE_WORKLOADS + wl.EXTRA + wl.PREFILL:
             if other.name == spec.name:
                 continue
             # as many steps as the main workload (a replay of a few hundred steps still

@@ -48,9 +48,9 @@ class Spec:
     ring: bool = False            # circular-buffer state: cache_seqlens drawn U{0..4095}
 
 
-# The five synthetic configurations.  Index 0 is the tiny case, 3 is the large
+# The five synthetic decode workloads.  Index 0 is the tiny case, 3 is the large
 # decode batch the benchmark times.
-CONFIGS = [
+DECODE_WORKLOADS = [
     Spec("tiny", N=4, D=64, W=4, L=3, S=4, ld=64, bias=False, act=None,
          routing="none", seed=1),
     Spec("page_shaped", N=8, D=2048, W=4, L=4, S=8, ld=2048, bias=True, act="silu",
@@ -82,7 +82,7 @@ EXTRA = [
     Spec("large_decode_ring_4tok", N=256, D=8192, W=4, L=3, S=256, ld=8200, bias=False, act="silu",
          routing="none", T=4, weight_dist="uniform", seed=4, layout="channel_last", ring=True, one_call=True),
 ]
-BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
+BY_NAME = {c.name: c for c in DECODE_WORKLOADS + EXTRA}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

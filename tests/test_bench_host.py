@@ -48,7 +48,7 @@ def test_tokens_scale_x_and_out_but_not_state():
 
 
 def test_workload_shapes_and_padding():
-    for spec in wl.CONFIGS + wl.EXTRA:
+    for spec in wl.DECODE_WORKLOADS + wl.EXTRA:
         if spec.N * spec.D * spec.T > 4_000_000:
             continue
         d = wl.make(spec)

@@ -63,7 +63,7 @@ def _gpu():
 # ------------------------------------------------------------ the five workloads
 
 
-@pytest.mark.parametrize("spec", wl.CONFIGS[:4], ids=[c.name for c in wl.CONFIGS[:4]])
+@pytest.mark.parametrize("spec", wl.DECODE_WORKLOADS[:4], ids=[c.name for c in wl.DECODE_WORKLOADS[:4]])
 def test_configs_single_step(spec):
     data = wl.make(spec)
     case = Case(data["x"][0], spec.D, data["weight"], data["state"], bias=data["bias"],
