@@ -34,17 +34,20 @@ __device__ __forceinline__ int ring_pos(int t, int L) {
     return r < 0 ? r + L : r;
 }
 
-// The row's slot, or -1 when it must not touch the state; a negative
-// cache_seqlens entry rejects the row and sets DCCONV_DEV_BAD_SEQLEN.  All 64
-// lanes of the wave call it; the result is wave-uniform.
+// A routed row's slot after the count check: a negative cache_seqlens entry
+// rejects the row (-1) and sets DCCONV_DEV_BAD_SEQLEN.  All 64 lanes of the
+// wave call it; the result is wave-uniform.
+__device__ __forceinline__ int ring_reject(int32_t *status, int slot, int seen, int lane) {
+    if (seen >= 0) return slot;
+    if (status != nullptr && lane == 0) atomicOr(status, DCCONV_DEV_BAD_SEQLEN);
+    return -1;
+}
+
+// The row's slot (or -1 when it must not touch the state) and its count.
 __device__ __forceinline__ int route_ring_row(const UpdateParams &p, int row, int lane, int *seen) {
     const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
     *seen = p.seqlens[row];
-    if (*seen < 0) {
-        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQLEN);
-        return -1;
-    }
-    return slot;
+    return ring_reject(p.status, slot, *seen, lane);
 }
 
 // L3: the ring holds exactly the W-1 = 3 taps, so every plane is read whatever
@@ -67,13 +70,18 @@ __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int til
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
         const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
 
-        int slot[R], head[R];  // head: ring position of the newest slot value + 1 (= c mod L)
+        // The rows' counts, all requested before any is examined (scalar loads:
+        // one round trip for the wave), then their slots.
+        int seen[R], slot[R], head[R];  // head: ring position of the newest slot value + 1 (= c mod L)
+#pragma unroll
+        for (int r = 0; r < R; ++r) seen[r] = load_uniform(p.seqlens, min(group * R + r, p.n - 1));
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = group * R + r;
-            int c = 0;
-            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_ring_row(p, row, lane, &c) : -2);
-            head[r] = __builtin_amdgcn_readfirstlane(c) % (L3 ? 3 : L);  // c >= 0 for a live row
+            slot[r] = __builtin_amdgcn_readfirstlane(
+                row < p.n ? ring_reject(p.status, route_row(p.idx, p.status, p.n, p.s, row, lane), seen[r], lane)
+                          : -2);
+            head[r] = (seen[r] < 0 ? 0 : seen[r]) % (L3 ? 3 : L);  // seen >= 0 for a live row
         }
 
         // every load up front: weights, bias, then each row's x and tap planes
@@ -187,11 +195,7 @@ constexpr uint32_t kBadToken = 1u << 30;  // beyond every descriptor here (all <
 __device__ __forceinline__ int route_ring_tokens_row(const TokensParams &p, int row, int lane, int *seen) {
     const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
     *seen = p.seqlens[row];
-    if (*seen < 0) {
-        if (p.status != nullptr && lane == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQLEN);
-        return -1;
-    }
-    return slot;
+    return ring_reject(p.status, slot, *seen, lane);
 }
 
 // R rows per wave, KP tokens per pass; L3: the ring holds exactly the three
