@@ -135,6 +135,28 @@ def test_ring_padding_bad_and_duplicate_rows():
     assert status == dc.DCCONV_DEV_BAD_INDEX | dc.DCCONV_DEV_DUP_INDEX | dc.DCCONV_DEV_BAD_SEQLEN
 
 
+def test_ring_two_rows_per_wave_rejections():
+    """Negative counts, padding and bad indices in the two-rows-per-wave kernel:
+    rejected rows are zero and leave their slots alone, whichever row of its wave
+    they are."""
+    case = RingCase(3250, N=256, D=4096, L=3, S=300, routing="padded", n_pad=20, status=True, max_seen=5000)
+    case.indices = case.indices.copy()
+    live = np.flatnonzero(case.indices >= 0)
+    case.seqlens = case.seqlens.copy()
+    neg = live[[3, 4, 50, 51, 200]]                    # both rows of some waves, one row of others
+    case.seqlens[neg] = -1 - np.arange(len(neg), dtype=np.int32)
+    case.indices[live[100]] = 300                      # out of range
+    oi = case.indices.copy()
+    oi[neg] = -1
+    oi[live[100]] = -1
+    case.oracle_indices = oi
+    cs = case.seqlens.copy(); cs[neg] = 0              # the oracle refuses negatives; those rows are padding
+    case.oracle_seqlens = cs
+    status = case.check()
+    assert status == dc.DCCONV_DEV_BAD_INDEX | dc.DCCONV_DEV_BAD_SEQLEN
+    assert case.kernel == "update_ring_v8<silu,R=2>", case.kernel
+
+
 def test_ring_full_size_large_decode():
     """The large decode batch (N=256, D=8192, L=3, SiLU, x row stride 8200) on a
     channel-last ring, element by element."""
