@@ -77,6 +77,19 @@ __device__ __forceinline__ float activate<DCCONV_ACT_SILU>(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * kMinusLog2e));
 }
 
+// Calls body(u) for the units u = blockIdx.x, blockIdx.x + gridDim.x, ... below
+// `units`.  Every launch has at least one unit per block, so the first call needs
+// no test: the kernel's arguments are then all requested at once, one round trip
+// before the first load instead of two.
+template <typename Body>
+__device__ __forceinline__ void for_each_unit(int64_t units, Body &&body) {
+    int64_t u = blockIdx.x;
+    do {
+        body(u);
+        u += gridDim.x;
+    } while (u < units);
+}
+
 // Orders this wave's LDS accesses across lanes.  LDS instructions of one
 // wavefront execute in order, so wavefront-scope fences (which keep the compiler
 // from moving LDS accesses across this point) are all that is needed.

@@ -568,12 +568,15 @@ __global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles,
     __shared__ u32x4 stage_all[kWavesPerBlock * kWave * L];
     __shared__ u32x4 weight_tile[4 * kWave];
     const int64_t total = edge_blocks + chunk_blocks;
-    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    // the launch never has more blocks than units, so the first needs no test
+    int64_t b = blockIdx.x;
+    do {
         if (b < edge_blocks)
             edge_block<L, ACT, LAYOUT, kWavesPerBlock>(p, stage_all, weight_tile, tiles, b);
         else
             chunk_block<ACT, HAS_BIAS>(p, weight_tile, tiles, chunk, units, units_per_seq, b - edge_blocks);
-    }
+        b += gridDim.x;
+    } while (b < total);
 }
 
 // The sweep form of the same call: `grid` sweep blocks and `edge_blocks` edge
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(kSweepBlock) void prefill_sweep_v8(PrefillParams p,
 template <int ACT>
 __global__ __launch_bounds__(kScalarBlock) void prefill_scalar(PrefillParams p, int tiles_per_seq, int64_t units) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for_each_unit(units, [&](int64_t unit) {
         const int i = (int)(unit / tiles_per_seq);
         const int c = (int)(unit - (int64_t)i * tiles_per_seq) * kScalarBlock + (int)threadIdx.x;
         int a = 0, e = p.t;
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(kScalarBlock) void prefill_scalar(PrefillParams p, 
             if (!ok && p.status != nullptr && threadIdx.x == 0) atomicOr(p.status, DCCONV_DEV_BAD_SEQ);
         }
         const int slot = ok ? route_row(p.idx, p.status, p.n, p.s, i, lane) : -2;
-        if (c >= p.d || !ok) continue;
+        if (c >= p.d || !ok) return;
         const int len = e - a;
         const uint16_t *xc = (p.starts != nullptr ? p.x + (int64_t)a * p.xs_t : p.x + (int64_t)i * p.xs_n) +
                              (int64_t)c * p.xs_d;
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(kScalarBlock) void prefill_scalar(PrefillParams p, 
                        (int64_t)c * p.os_d;
         if (slot < 0) {  // padding (or rejected) sequence
             for (int j = 0; j < len; ++j) oc[(int64_t)j * p.os_t] = 0;
-            continue;
+            return;
         }
         const bool stateful = p.state != nullptr;
         const bool from_state = stateful && p.has_init != nullptr && p.has_init[i] != 0;
@@ -655,7 +658,7 @@ __global__ __launch_bounds__(kScalarBlock) void prefill_scalar(PrefillParams p, 
                 h[(int64_t)k * sl] = v;
             }
         }
-    }
+    });
 }
 
 template <typename Kernel, typename... Args>

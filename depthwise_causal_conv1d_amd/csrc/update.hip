@@ -106,7 +106,9 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
     // A block owns one 512-channel tile and kWavesPerBlock groups of R rows, one
     // group per wave, so the tile's weights are fetched once per block with
     // coalesced loads and shared through LDS.
-    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+    // the launch never has more blocks than units, so the first needs no test
+    int64_t bu = blockIdx.x;
+    do {
         const int tile = (int)(bu % tiles_per_row);
         const int group = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -203,7 +205,8 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             buffer_store<kStream>(ov[r], obuf[r], lane_bytes);
         }
         __syncthreads();  // the stages and the weight tile are reused by the next unit
-    }
+        bu += gridDim.x;
+    } while (bu < block_units);
 }
 
 template <int L, int ACT, int R, bool HAS_BIAS>
@@ -219,7 +222,9 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const uint32_t plane_bytes = (uint32_t)p.st_l * 2u;  // distance between history positions
 
-    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+    // the launch never has more blocks than units, so the first needs no test
+    int64_t bu = blockIdx.x;
+    do {
         const int tile = (int)(bu % tiles_per_row);
         const int group = (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -297,21 +302,22 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
             buffer_store<kStream>(ov[r], obuf[r], lane_bytes);
         }
         __syncthreads();  // the weight tile is reused by the next unit
-    }
+        bu += gridDim.x;
+    } while (bu < block_units);
 }
 
 template <int ACT>
 __global__ __launch_bounds__(kScalarBlock) void update_scalar(UpdateParams p, int tiles_per_row, int64_t units) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for_each_unit(units, [&](int64_t unit) {
         const int row = (int)(unit / tiles_per_row);
         const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
         const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
-        if (c >= p.d) continue;
+        if (c >= p.d) return;
         uint16_t *o = p.out + (int64_t)row * p.d + c;
         if (slot < 0) {
             *o = 0;
-            continue;
+            return;
         }
         const int L = p.l;
         uint16_t *h = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kScalarBlock) void update_scalar(UpdateParams p, in
         acc = __builtin_fmaf(bf16_bits_to_f32(x), bf16_bits_to_f32(wt[3]), acc);
         if (p.bias != nullptr) acc += bf16_bits_to_f32(p.bias[c]);
         *o = f32_to_bf16_bits(activate<ACT>(acc));
-    }
+    });
 }
 
 // Launches `units` block units (the kernels stride over them when the grid is capped).

@@ -62,7 +62,9 @@ __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int til
     const int L = p.l;
 
     // A block owns one 512-channel tile and kWavesPerBlock groups of R rows.
-    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+    // the launch never has more blocks than units, so the first needs no test
+    int64_t bu = blockIdx.x;
+    do {
         const int tile = (int)(bu % tiles);
         const int group = (int)(bu / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -138,22 +140,23 @@ __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int til
             buffer_store<kStream>(xv[r], sbuf[r], plane_bytes * (uint32_t)head[r] + lane_off);
         }
         __syncthreads();  // the weight tile is reused by the next unit
-    }
+        bu += gridDim.x;
+    } while (bu < block_units);
 }
 
 template <int ACT>
 __global__ __launch_bounds__(kScalarBlock) void update_ring_scalar(UpdateParams p, int tiles_per_row, int64_t units) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for_each_unit(units, [&](int64_t unit) {
         const int row = (int)(unit / tiles_per_row);
         const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
         int seen = 0;
         const int slot = route_ring_row(p, row, lane, &seen);
-        if (c >= p.d) continue;
+        if (c >= p.d) return;
         uint16_t *o = p.out + (int64_t)row * p.d + c;
         if (slot < 0) {
             *o = 0;
-            continue;
+            return;
         }
         const int L = p.l;
         uint16_t *ring = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kScalarBlock) void update_ring_scalar(UpdateParams 
         if (p.bias != nullptr) acc += bf16_bits_to_f32(p.bias[c]);
         *o = f32_to_bf16_bits(activate<ACT>(acc));
         ring[(int64_t)ring_pos(seen, L) * sl] = xb;
-    }
+    });
 }
 
 template <typename Kernel>
@@ -210,7 +213,9 @@ __global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int til
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
     const int L = L3 ? 3 : p.l;
 
-    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+    // the launch never has more blocks than units, so the first needs no test
+    int64_t bu = blockIdx.x;
+    do {
         const int tile = (int)(bu % tiles);
         const int group = (int)(bu / tiles) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -310,22 +315,23 @@ __global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int til
                 }
         }
         __syncthreads();  // the weight tile is reused by the next unit
-    }
+        bu += gridDim.x;
+    } while (bu < block_units);
 }
 
 template <int ACT>
 __global__ __launch_bounds__(kScalarBlock) void tokens_ring_scalar(TokensParams p, int tiles_per_row, int64_t units) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for_each_unit(units, [&](int64_t unit) {
         const int row = (int)(unit / tiles_per_row);
         const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
         int seen = 0;
         const int slot = route_ring_tokens_row(p, row, lane, &seen);
-        if (c >= p.d) continue;
+        if (c >= p.d) return;
         uint16_t *o = p.out + (int64_t)row * p.os_n + (int64_t)c * p.os_d;
         if (slot < 0) {
             for (int t = 0; t < p.t; ++t) o[(int64_t)t * p.os_t] = 0;
-            continue;
+            return;
         }
         const int L = p.l;
         uint16_t *ring = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(kScalarBlock) void tokens_ring_scalar(TokensParams 
             h1 = h2;
             h2 = xv;
         }
-    }
+    });
 }
 
 template <typename Kernel>

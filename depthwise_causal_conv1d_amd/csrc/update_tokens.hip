@@ -64,7 +64,9 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
     const int te = (SPLIT && wave == 0) ? p.t / 2 : p.t;
     const bool reads_state = !SPLIT || wave == 0;
     const bool writes_state = !SPLIT || wave == 1;
-    for (int64_t bu = blockIdx.x; bu < block_units; bu += gridDim.x) {
+    // the launch never has more blocks than units, so the first needs no test
+    int64_t bu = blockIdx.x;
+    do {
         const int tile = (int)(bu % tiles_per_row);
         const int group = SPLIT ? (int)(bu / tiles_per_row) : (int)(bu / tiles_per_row) * kWavesPerBlock + wave;
         const int c0 = tile * kChPerWave;
@@ -265,21 +267,22 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
             }
         }
         __syncthreads();  // the stage and the weight tile are reused by the next unit
-    }
+        bu += gridDim.x;
+    } while (bu < block_units);
 }
 
 template <int ACT>
 __global__ __launch_bounds__(kScalarBlock) void tokens_scalar(TokensParams p, int tiles_per_row, int64_t units) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for_each_unit(units, [&](int64_t unit) {
         const int row = (int)(unit / tiles_per_row);
         const int c = (int)(unit - (int64_t)row * tiles_per_row) * kScalarBlock + (int)threadIdx.x;
         const int slot = route_row(p.idx, p.status, p.n, p.s, row, lane);
-        if (c >= p.d) continue;
+        if (c >= p.d) return;
         uint16_t *o = p.out + (int64_t)row * p.os_n + (int64_t)c * p.os_d;
         if (slot < 0) {
             for (int t = 0; t < p.t; ++t) o[(int64_t)t * p.os_t] = 0;
-            continue;
+            return;
         }
         const int L = p.l;
         uint16_t *h = p.state + (int64_t)slot * p.st_s + (int64_t)c * p.st_d;
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(kScalarBlock) void tokens_scalar(TokensParams p, in
             if (p.bias != nullptr) acc += b;
             o[(int64_t)t * p.os_t] = f32_to_bf16_bits(activate<ACT>(acc));
         }
-    }
+    });
 }
 
 template <typename Kernel>
