@@ -15,7 +15,7 @@ constexpr int kChPerWave = kWave * kChPerLane;  // 512 channels
 constexpr int kWavesPerBlock = 2;
 constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kScalarBlock = 256;               // channels per block in the scalar path
-constexpr int64_t kMaxBlocks = 1 << 20;         // grid cap; the kernels stride over units
+constexpr int64_t kMaxBlocks = 1 << 20;         // grid cap: min(units, kMaxBlocks) blocks, stride kMaxBlocks
 // Two rows per wave once the grid still has this many waves: fewer, fuller waves
 // keep more bytes in flight per wave and share one weight load between rows.
 constexpr int64_t kMinWavesForTwoRows = 1024;
@@ -77,16 +77,18 @@ __device__ __forceinline__ float activate<DCCONV_ACT_SILU>(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * kMinusLog2e));
 }
 
-// Calls body(u) for the units u = blockIdx.x, blockIdx.x + gridDim.x, ... below
-// `units`.  Every launch has at least one unit per block, so the first call needs
-// no test: the kernel's arguments are then all requested at once, one round trip
-// before the first load instead of two.
+// Calls body(u) for the units u = blockIdx.x, blockIdx.x + kMaxBlocks, ... below
+// `units`.  Every kernel here is launched with min(units, kMaxBlocks) blocks, so
+// the first unit needs no test and the stride is the constant kMaxBlocks (one
+// pass when units <= kMaxBlocks).  Neither the unit count nor the grid size is
+// then needed before the first load: every kernel argument is requested at
+// once, one round trip instead of two.
 template <typename Body>
 __device__ __forceinline__ void for_each_unit(int64_t units, Body &&body) {
     int64_t u = blockIdx.x;
     do {
         body(u);
-        u += gridDim.x;
+        u += kMaxBlocks;
     } while (u < units);
 }
 

@@ -568,14 +568,14 @@ __global__ __launch_bounds__(kBlock) void prefill_v8(PrefillParams p, int tiles,
     __shared__ u32x4 stage_all[kWavesPerBlock * kWave * L];
     __shared__ u32x4 weight_tile[4 * kWave];
     const int64_t total = edge_blocks + chunk_blocks;
-    // the launch never has more blocks than units, so the first needs no test
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
     int64_t b = blockIdx.x;
     do {
         if (b < edge_blocks)
             edge_block<L, ACT, LAYOUT, kWavesPerBlock>(p, stage_all, weight_tile, tiles, b);
         else
             chunk_block<ACT, HAS_BIAS>(p, weight_tile, tiles, chunk, units, units_per_seq, b - edge_blocks);
-        b += gridDim.x;
+        b += kMaxBlocks;
     } while (b < total);
 }
 

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
     // A block owns one 512-channel tile and kWavesPerBlock groups of R rows, one
     // group per wave, so the tile's weights are fetched once per block with
     // coalesced loads and shared through LDS.
-    // the launch never has more blocks than units, so the first needs no test
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
     int64_t bu = blockIdx.x;
     do {
         const int tile = (int)(bu % tiles_per_row);
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             buffer_store<kStream>(ov[r], obuf[r], lane_bytes);
         }
         __syncthreads();  // the stages and the weight tile are reused by the next unit
-        bu += gridDim.x;
+        bu += kMaxBlocks;
     } while (bu < block_units);
 }
 
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
     const uint32_t lane_bytes = (uint32_t)lane * 16u;
     const uint32_t plane_bytes = (uint32_t)p.st_l * 2u;  // distance between history positions
 
-    // the launch never has more blocks than units, so the first needs no test
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
     int64_t bu = blockIdx.x;
     do {
         const int tile = (int)(bu % tiles_per_row);
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
             buffer_store<kStream>(ov[r], obuf[r], lane_bytes);
         }
         __syncthreads();  // the weight tile is reused by the next unit
-        bu += gridDim.x;
+        bu += kMaxBlocks;
     } while (bu < block_units);
 }
 

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int til
     const int L = p.l;
 
     // A block owns one 512-channel tile and kWavesPerBlock groups of R rows.
-    // the launch never has more blocks than units, so the first needs no test
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
     int64_t bu = blockIdx.x;
     do {
         const int tile = (int)(bu % tiles);
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int til
             buffer_store<kStream>(xv[r], sbuf[r], plane_bytes * (uint32_t)head[r] + lane_off);
         }
         __syncthreads();  // the weight tile is reused by the next unit
-        bu += gridDim.x;
+        bu += kMaxBlocks;
     } while (bu < block_units);
 }
 
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int til
     const uint32_t x_tok = (uint32_t)p.xs_t * 2u, o_tok = (uint32_t)p.os_t * 2u, plane_bytes = (uint32_t)p.st_l * 2u;
     const int L = L3 ? 3 : p.l;
 
-    // the launch never has more blocks than units, so the first needs no test
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
     int64_t bu = blockIdx.x;
     do {
         const int tile = (int)(bu % tiles);
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int til
                 }
         }
         __syncthreads();  // the weight tile is reused by the next unit
-        bu += gridDim.x;
+        bu += kMaxBlocks;
     } while (bu < block_units);
 }
 

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
     const int te = (SPLIT && wave == 0) ? p.t / 2 : p.t;
     const bool reads_state = !SPLIT || wave == 0;
     const bool writes_state = !SPLIT || wave == 1;
-    // the launch never has more blocks than units, so the first needs no test
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
     int64_t bu = blockIdx.x;
     do {
         const int tile = (int)(bu % tiles_per_row);
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
             }
         }
         __syncthreads();  // the stage and the weight tile are reused by the next unit
-        bu += gridDim.x;
+        bu += kMaxBlocks;
     } while (bu < block_units);
 }
 
