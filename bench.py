@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -43,17 +44,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, blank lines and runs of white space (an edit
+    of those leaves the compiled kernel, and so its counters, unchanged)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the sources a kernel is compiled from (its file and the shared
-    device helpers), so stale counter summaries are recognised."""
+    """Hash of the code a kernel is compiled from (its file and the shared device
+    helpers, comments left out), so stale counter summaries are recognised."""
     main = ("update_ring.hip" if kernel.startswith("tokens_ring") else
             "update_tokens.hip" if kernel.startswith("tokens_") else
             "prefill.hip" if kernel.startswith("prefill_") else
             "update_ring.hip" if kernel.startswith("update_ring") else "update.hip")
     h = hashlib.sha256()
     for name in (main, "device_common.h"):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -50,8 +50,9 @@ __device__ __forceinline__ int route_ring_row(const UpdateParams &p, int row, in
     return ring_reject(p.status, slot, *seen, lane);
 }
 
-// L3: the ring holds exactly the W-1 = 3 taps, so every plane is read whatever
-// the count, and the loads need not wait for it: tap k is plane (c + k) mod 3.
+// L3: the ring holds exactly the W-1 = 3 taps, so the three planes are read in
+// plane order whatever the count and rotated afterwards (tap k is plane
+// (c + k) mod 3): no load offset depends on the count.
 template <int ACT, int R, bool HAS_BIAS, bool L3>
 __global__ __launch_bounds__(kBlock) void update_ring_v8(UpdateParams p, int tiles, int64_t block_units) {
     __shared__ u32x4 weight_tile[4 * kWave];
@@ -202,8 +203,8 @@ __device__ __forceinline__ int route_ring_tokens_row(const TokensParams &p, int 
 }
 
 // R rows per wave, KP tokens per pass; L3: the ring holds exactly the three
-// taps, so its planes are loaded in plane order before the count arrives and
-// rotated by c mod 3 afterwards (as in update_ring_v8).
+// taps, so its planes are loaded in plane order and rotated by c mod 3
+// afterwards (as in update_ring_v8).
 template <int ACT, bool HAS_BIAS, int R, int KP, bool L3>
 __global__ __launch_bounds__(kBlock) void tokens_ring_v8(TokensParams p, int tiles, int64_t block_units) {
     __shared__ u32x4 weight_tile[4 * kWave];

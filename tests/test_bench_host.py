@@ -127,3 +127,12 @@ def test_ring_tokens_bytes_by_hand():
     N, D, T, L = 256, 8192, 4, 3
     hand = 2 * N * D * T + 2 * N * D * 3 + 2 * N * D * min(T, L) + 2 * N * D * T + 2 * D * 4 + 4 * N
     assert wl.algorithmic_bytes(N, D, 4, L, N, False, False, "channel_last", T, ring=True) == hand
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    """A comment edit keeps a counter summary current; a code edit makes it stale."""
+    import bench
+    code = "int f(int a) {  // adds one\n    /* the\n  sum */ return a + 1;\n}\n"
+    assert bench._code_only(code) == bench._code_only(code.replace("adds one", "increments"))
+    assert bench._code_only(code) == bench._code_only("int f(int a) {\n\n    return a + 1;\n}\n")
+    assert bench._code_only(code) != bench._code_only(code.replace("a + 1", "a + 2"))
