@@ -62,12 +62,19 @@ _lock = threading.Lock()
 _lib = None
 
 
+# The test of planted mistakes points this at a deliberately broken build of the
+# oracle, to show that the pins catch each mistake; nothing else sets it.
+_LIBRARY_ENV = "DCCONV_ORACLE_LIBRARY"
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            L = ctypes.CDLL(_LIB)
+            other = os.environ.get(_LIBRARY_ENV)
+            if not other:
+                build()
+            L = ctypes.CDLL(other or _LIB)
             i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
             L.oracle_update.restype = i32
             L.oracle_update.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64,
@@ -90,6 +97,10 @@ def lib() -> ctypes.CDLL:
             L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
             L.oracle_f32_to_bf16.restype = ctypes.c_uint16
             L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+            L.oracle_bf16_to_f32_bits.restype = ctypes.c_uint32
+            L.oracle_bf16_to_f32_bits.argtypes = [ctypes.c_uint16]
+            L.oracle_f32_bits_to_bf16.restype = ctypes.c_uint16
+            L.oracle_f32_bits_to_bf16.argtypes = [ctypes.c_uint32]
             L.oracle_version.restype = i32
             _lib = L
     return _lib
@@ -107,17 +118,19 @@ def _need(a, dtype, name):
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
-    """Element-wise oracle BF16 -> FP32 (slow; for pinning the converter)."""
-    f = lib().oracle_bf16_to_f32
+    """Element-wise oracle BF16 -> FP32 (slow; for pinning the converter).  Bit
+    patterns cross the binding, so NaN payloads arrive unchanged."""
+    f = lib().oracle_bf16_to_f32_bits
     flat = np.asarray(bits, dtype=np.uint16).ravel()
-    return np.array([f(int(b)) for b in flat], dtype=np.float32).reshape(np.shape(bits))
+    return np.array([f(int(b)) for b in flat], dtype=np.uint32).view(np.float32).reshape(np.shape(bits))
 
 
 def f32_to_bf16(vals: np.ndarray) -> np.ndarray:
-    """Element-wise oracle FP32 -> BF16 bits, round to nearest even (slow)."""
-    f = lib().oracle_f32_to_bf16
-    flat = np.asarray(vals, dtype=np.float32).ravel()
-    return np.array([f(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(vals))
+    """Element-wise oracle FP32 -> BF16 bits, round to nearest even (slow).  Bit
+    patterns cross the binding, so a signalling NaN reaches the converter as it is."""
+    f = lib().oracle_f32_bits_to_bf16
+    flat = np.asarray(vals, dtype=np.float32).ravel().view(np.uint32)
+    return np.array([f(int(v)) for v in flat], dtype=np.uint16).reshape(np.shape(vals))
 
 
 def update(x, conv_state, weight, bias=None, activation=None, *, conv_state_indices=None,

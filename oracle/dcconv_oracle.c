@@ -63,6 +63,24 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+/* The two conversions on bit patterns, for callers that cannot pass an FP32
+ * value unchanged (a float handed through a double, as a scripting-language
+ * binding does, turns a signalling NaN quiet). */
+uint32_t oracle_bf16_to_f32_bits(uint16_t b)
+{
+    float f = oracle_bf16_to_f32(b);
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+uint16_t oracle_f32_bits_to_bf16(uint32_t bits)
+{
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return oracle_f32_to_bf16(f);
+}
+
 int oracle_update_tokens(const uint16_t *x, int64_t n_rows, int64_t d, int64_t t_steps,
                          int64_t xs_n, int64_t xs_d, int64_t xs_t,
                          uint16_t *state, int64_t s_slots, int64_t l,

@@ -15,6 +15,8 @@
 
 float oracle_bf16_to_f32(uint16_t b);
 uint16_t oracle_f32_to_bf16(float f);
+uint32_t oracle_bf16_to_f32_bits(uint16_t b);
+uint16_t oracle_f32_bits_to_bf16(uint32_t bits);
 int oracle_update(const uint16_t *x, int64_t n_rows, int64_t d, int64_t ld, uint16_t *state, int64_t s_slots,
                   int64_t l, int64_t st_s, int64_t st_d, int64_t st_l, const uint16_t *weight, int64_t w,
                   const uint16_t *bias, const int32_t *indices, int activation, uint16_t *out, float *out_f32);
@@ -59,6 +61,8 @@ int main(void) {
     const float vals[] = {0.0f, -0.0f, 1e-45f, 3.4e38f, -3.4e38f, 1.0f / 0.0f};
     for (int i = 0; i < 6; ++i) (void)oracle_bf16_to_f32(oracle_f32_to_bf16(vals[i]));
     for (uint32_t b = 0; b < 65536u; b += 97u) (void)oracle_f32_to_bf16(oracle_bf16_to_f32((uint16_t)b));
+    for (uint32_t b = 0; b < 65536u; b += 97u)
+        (void)oracle_f32_bits_to_bf16(oracle_bf16_to_f32_bits((uint16_t)b) | 1u);
 
     for (int64_t l = 3; l <= 9; l += 3) {
         const int64_t n = 5, d = 7, s = 8, w = 4, t = 6, ld = 9;

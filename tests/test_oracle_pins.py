@@ -71,12 +71,11 @@ def check_out(out_bits, out_f32, exact_acc, abs_terms, act):
 
 
 def test_bf16_to_f32_all_patterns():
+    # every pattern, NaN payloads and signalling NaNs included, bit for bit
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     ours = oracle.bf16_to_f32(bits)
     lib = bf16_bits_to_f32(bits)
-    nan = np.isnan(lib)
-    assert np.array_equal(np.isnan(ours), nan)
-    np.testing.assert_array_equal(ours.view(np.uint32)[~nan], lib.view(np.uint32)[~nan])
+    np.testing.assert_array_equal(ours.view(np.uint32), lib.view(np.uint32))
 
 
 def test_f32_to_bf16_matches_library_rne():
@@ -97,9 +96,14 @@ def test_f32_to_bf16_matches_library_rne():
 
 
 def test_f32_to_bf16_nan_stays_nan():
-    nans = np.array([0x7FC00000, 0x7F800001, 0xFFC00001, 0x7FFFFFFF], dtype=np.uint32).view(np.float32)
+    # quiet and signalling NaNs, with payloads in the kept and in the dropped half
+    nans = np.array([0x7FC00000, 0x7F800001, 0xFF800001, 0xFFC00001, 0x7FFFFFFF, 0x7F810000],
+                    dtype=np.uint32).view(np.float32)
     out = oracle.f32_to_bf16(nans)
     assert np.all(np.isnan(bf16_bits_to_f32(out)))
+    # the sign survives, and a payload in the kept half is kept
+    np.testing.assert_array_equal(out >> 15, [0, 0, 1, 1, 0, 0])
+    assert out[5] & 0x003F == 0x0001  # below the quiet bit, which is forced on
 
 
 # ------------------------------------------------------------------- golden cases
