@@ -59,7 +59,8 @@ enum {
     DCCONV_DEV_DUP_INDEX = 2, /* two rows of the batch select one real slot  */
     DCCONV_DEV_BAD_SEQ = 4,   /* dcconv_prefill: seq_starts is not 0 = starts[0]
                                  <= starts[1] <= ... <= starts[n] = t          */
-    DCCONV_DEV_BAD_SEQLEN = 8 /* dcconv_update: a cache_seqlens entry below 0  */
+    DCCONV_DEV_BAD_SEQLEN = 8 /* dcconv_update, dcconv_update_tokens: a
+                                 cache_seqlens entry below 0                  */
 };
 
 /* The DCCONV_ABI_VERSION the library was built with. */
