@@ -246,5 +246,42 @@ __device__ __forceinline__ u32x4 conv8(const u32x4 &h0, const u32x4 &h1, const u
     return u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
 }
 
+
+// ---- host side: the launch shape of the one-token kernels --------------------
+
+// Compute units of the current device (cached per device; 0 if unknown).
+constexpr int kMaxCachedDevices = 64;
+inline int64_t device_cu_count() {
+    static int cache[kMaxCachedDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxCachedDevices) {
+        const int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    if (dev < kMaxCachedDevices) __atomic_store_n(&cache[dev], cus, __ATOMIC_RELAXED);
+    return cus;
+}
+
+// Whether the one-token kernels take two rows per wave for n rows of `tiles`
+// 512-channel tiles.  Only when the grid keeps kMinWavesForTwoRows waves, and
+// only when the blocks, spread over the CUs in whole rounds, do not cost more
+// rounds x rows than one row per wave would: with C CUs, ceil(blocks_2 / C) * 2
+// against ceil(blocks_1 / C).  (N = 160, D = 8192: 640 two-row blocks in 3
+// rounds of 2 rows against 1280 one-row blocks in 5 rounds; 5.44 against
+// 5.06 us measured.  N = 256: 4 x 2 against 8, a tie, and two rows win:
+// 6.24 against 6.34-6.41 us.)
+inline bool two_rows_per_wave(int64_t n, int64_t tiles) {
+    const int64_t groups_two = (n + 1) / 2;
+    if (n < 2 || groups_two * tiles < kMinWavesForTwoRows) return false;
+    const int64_t cus = device_cu_count();
+    if (cus <= 0) return true;
+    const int64_t blocks_one = tiles * ((n + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int64_t blocks_two = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
+    return (blocks_two + cus - 1) / cus * 2 <= (blocks_one + cus - 1) / cus;
+}
+
 }  // namespace
 }  // namespace dcconv

@@ -354,7 +354,7 @@ hipError_t launch_compact_l(const UpdateParams &p, int tiles, hipStream_t stream
                             const char *name_one_row, const char *name_two_rows) {
     const bool bias = p.bias != nullptr;
     const int64_t groups_two = (p.n + 1) / 2;
-    if (p.n >= 2 && groups_two * tiles >= kMinWavesForTwoRows) {
+    if (two_rows_per_wave(p.n, tiles)) {
         *name = name_two_rows;
         const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
         return bias ? launch(update_compact_v8<L, ACT, 2, true>, p, tiles, block_units, kBlock, stream)
@@ -400,7 +400,7 @@ hipError_t launch_channel_last_l(const UpdateParams &p, int tiles, hipStream_t s
                                  const char *name_one_row, const char *name_two_rows) {
     const bool bias = p.bias != nullptr;
     const int64_t groups_two = (p.n + 1) / 2;
-    if (p.n >= 2 && groups_two * tiles >= kMinWavesForTwoRows) {
+    if (two_rows_per_wave(p.n, tiles)) {
         *name = name_two_rows;
         const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
         return bias ? launch(update_channel_last_v8<L, ACT, 2, true>, p, tiles, block_units, kBlock, stream)

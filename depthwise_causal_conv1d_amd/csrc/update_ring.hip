@@ -434,8 +434,7 @@ hipError_t launch_update_ring(const UpdateParams &p, StateLayout layout, int act
                     p.st_s % kChPerLane == 0 && (int64_t)p.l * p.st_l * 2 + 2 * kChPerWave < ((int64_t)1 << 30);
     if (v8) {
         const int tiles = (p.d + kChPerWave - 1) / kChPerWave;
-        // two rows per wave once the grid still fills the chip with them
-        const bool two = ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
+        const bool two = two_rows_per_wave(p.n, tiles);
         const int rows_per_block = kWavesPerBlock * (two ? 2 : 1);
         const int64_t units = ((int64_t)p.n + rows_per_block - 1) / rows_per_block * tiles;
         const bool l3 = p.l == 3;

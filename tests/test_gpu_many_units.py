@@ -27,9 +27,10 @@ from test_gpu_update import make_case
 pytestmark = pytest.mark.gpu
 
 GRID_CAP = 1 << 20
-# Vector kernels: two waves of two rows per block and one 512-channel tile at
-# D = 8, so 4 rows per block unit; the scalar kernels: one row per unit at D < 256.
-ROWS_V8 = 4 * GRID_CAP + 9
+# Vector kernels: one 512-channel tile at D = 8 and two waves of one or two
+# rows per block, so at least 2^20 + 256 block units; the scalar kernels: one
+# row per unit at D < 256.
+ROWS_V8 = 4 * GRID_CAP + 1024
 ROWS_SCALAR = GRID_CAP + 7
 
 
@@ -43,21 +44,21 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("layout,L,N,D,kernel", [("compact", 3, ROWS_V8, 8, "update_compact_v8<L=3,silu,R=2>"),
-                                                 ("channel_last", 4, ROWS_V8, 8, "update_channel_last_v8<L=4,silu,R=2>"),
+@pytest.mark.parametrize("layout,L,N,D,kernel", [("compact", 3, ROWS_V8, 8, "update_compact_v8<L=3,silu,R="),
+                                                 ("channel_last", 4, ROWS_V8, 8, "update_channel_last_v8<L=4,silu,R="),
                                                  ("compact", 3, ROWS_SCALAR, 7, "update_scalar<silu>")])
 def test_update_more_units_than_blocks(layout, L, N, D, kernel):
     case = make_case(5000 + L, N=N, D=D, L=L, layout=layout, bias=True)
     case.check()
-    assert case.kernel == kernel, case.kernel
+    assert case.kernel.startswith(kernel), case.kernel
 
 
-@pytest.mark.parametrize("N,D,kernel", [(ROWS_V8, 8, "update_ring_v8<silu,R=2>"),
+@pytest.mark.parametrize("N,D,kernel", [(ROWS_V8, 8, "update_ring_v8<silu,R="),
                                         (ROWS_SCALAR, 7, "update_ring_scalar<silu>")])
 def test_ring_more_units_than_blocks(N, D, kernel):
     case = RingCase(5100 + D, N, D, 3, max_seen=1000)
     case.check()
-    assert case.kernel == kernel, case.kernel
+    assert case.kernel.startswith(kernel), case.kernel
 
 
 @pytest.mark.parametrize("N,D,layout,kernel", [(ROWS_V8, 8, "compact", "tokens_v8<L=3,silu,compact,R=2>"),

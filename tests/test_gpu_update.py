@@ -136,10 +136,22 @@ def test_channel_last_more_l(L):
 def test_two_rows_per_wave_odd_n_padding_bias(layout, act):
     """N odd (the last wave has one row and one row past the end), padding rows
     inside row pairs, a bias, an index table, a ragged tile: the two-row kernels."""
-    case = make_case(330, N=131, D=8200, L=3, S=300, layout=layout, routing="padded", n_pad=17, bias=True, act=act,
+    case = make_case(330, N=151, D=8200, L=3, S=300, layout=layout, routing="padded", n_pad=17, bias=True, act=act,
                      status=True)
     assert case.check() == 0
     assert "R=2" in case.kernel, case.kernel
+
+
+@pytest.mark.parametrize("N,R", [(160, 1), (192, 2), (256, 2)])
+def test_rows_per_wave_follow_whole_rounds_of_blocks(N, R):
+    """At D = 8192 on 256 CUs: 160 rows take one row per wave (1280 blocks, 5
+    rounds) rather than two (640 blocks, 3 rounds of two rows); 192 and 256 rows
+    take two.  Results are the same either way."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the expected choice is worked out for 256 compute units")
+    case = make_case(340 + N, N=N, D=8192, L=3, bias=False, act="silu")
+    case.check()
+    assert case.kernel == f"update_compact_v8<L=3,silu,R={R}>", case.kernel
 
 
 def test_channel_last_full_size_large_decode():
