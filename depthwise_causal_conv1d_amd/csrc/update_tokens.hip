@@ -336,13 +336,15 @@ constexpr int64_t kMaxWavesForSplit = 2048;
 
 template <int ACT, bool CL>
 hipError_t launch_tokens_v8(const TokensParams &p, int tiles, hipStream_t stream, const char **name) {
-    // Two rows per wave when the history is short and the grid still fills the
-    // chip with them; else one row per wave, its tokens split over two waves
+    // Two rows per wave when the history is short and the blocks' whole rounds
+    // over the CUs cost no more than with one row (two_rows_per_wave; 4 tokens
+    // at D = 8192: 144 and 160 rows 8.8-8.9 -> 7.2-7.3 us, 208 and 224 rows
+    // 9.7-9.8 -> 9.2-9.3 us with one row); else one row per wave, its tokens split over two waves
     // when the grid is thin and the call long.  A wave with 5 to 8 tokens takes
     // them in one pass of 8; a longer one-row wave goes in passes of 4 with the
     // next pass in flight, a longer two-row wave in passes of 4 loaded at their
     // start.  Every form stays within 256 registers.
-    const bool two = p.l <= 4 && ((int64_t)p.n + 1) / 2 * tiles >= kMinWavesForTwoRows;
+    const bool two = p.l <= 4 && two_rows_per_wave(p.n, tiles);
     const bool split = !two && (int64_t)p.n * tiles < kMaxWavesForSplit && p.t >= 2 * p.l;
     const int per_wave = split ? p.t - p.t / 2 : p.t;
     const bool one_pass = per_wave > 4 && per_wave <= 8;

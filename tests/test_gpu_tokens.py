@@ -200,8 +200,8 @@ def test_tokens_full_size_large_decode(layout, T):
 def test_tokens_two_rows_per_wave(layout, T):
     """Enough rows for two per wave: odd N (a lone last row), padding rows,
     bias, L = 4, token counts that leave a partial pass of 4."""
-    case = TokensCase(1450 + T, N=129, D=8192, T=T, L=4, layout=layout, bias=True, routing="padded", n_pad=9,
-                      S=160, status=True)
+    case = TokensCase(1450 + T, N=191, D=8192, T=T, L=4, layout=layout, bias=True, routing="padded", n_pad=9,
+                      S=200, status=True)
     assert case.check() == 0
     assert case.kernel == f"tokens_v8<L=4,silu,{layout}," + _two_row_form(T), case.kernel
 
