@@ -11,11 +11,22 @@ Cold-cache timing: the working set of one call (about 21 MB) fits in the 256 MB
 Infinity Cache, so consecutive steps cycle through enough independent buffer sets
 (x, state, weight, output) to exceed it; every step then reads from HBM.
 
-The timed region is K steps captured in one HIP graph and replayed once,
-bracketed by synchronisations and timed with HIP events on the stream that
-launches the kernels.  Achieved bandwidth is the algorithmic byte count of a call
-(x + selected state read + state write + weight + bias + output + index table)
-divided by the measured time per step.
+Timing: a timed region is exactly K steps, bracketed by device
+synchronisations and timed with HIP events (created without the system-scope
+fence, which the timed work does not need) on the stream that launches the
+kernels.  Up to 256 steps the region's launches go straight to the stream
+behind a spin kernel that holds the GPU until the host has enqueued them all,
+so the steps run back to back; a HIP graph replay would add a fixed 10-25 us
+per region here, half a microsecond per step at K = 20.  Longer regions are
+replayed from HIP graphs (several, when the buffer sets outnumber K, so the
+regions keep cycling through every set).  The per-step time reported is the
+median over the regions, with p10 and p90.  A plain copy of the same byte count
+(the library's measurement-control copy, same buffer rotation, same launch
+method) is timed interleaved with the update, region by region, as a control.
+
+Achieved bandwidth is the algorithmic byte count of a call (x + selected state
+read + state write + weight + bias + output + index table) divided by the
+median time per step.
 
 Prints exactly one JSON line on stdout; details go to stderr.
 """
@@ -197,7 +208,178 @@ class PrefillWorkload:
                          out=s["out"])
 
 
-def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
+class Head:
+    """A spin kernel enqueued ahead of a timed region: while the GPU spins, the
+    host finishes enqueueing the region's launches, so the start event is
+    followed directly by the first step and the steps run back to back.
+    Calibrated once; ``__call__(us)`` spins for about ``us`` microseconds."""
+
+    def __init__(self):
+        import torch
+
+        self.cycles_per_us = 0.0
+        if not hasattr(torch.cuda, "_sleep"):
+            return
+        probe = 200_000
+        stream = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(probe)
+        torch.cuda.synchronize()
+        a.record(stream)
+        torch.cuda._sleep(probe)
+        b.record(stream)
+        torch.cuda.synchronize()
+        self.cycles_per_us = probe / max(a.elapsed_time(b) * 1e3, 1e-3)
+
+    def __call__(self, us: float):
+        import torch
+
+        if self.cycles_per_us > 0:
+            torch.cuda._sleep(int(self.cycles_per_us * us))
+
+
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it
+    does not write back and invalidate the caches (a system-scope fence the
+    timed work does not need), which HIP documents as making timings between
+    events more precise.  The region is still closed by a device
+    synchronisation, which is a full fence."""
+
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(0x20000000))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self, stream):
+        import ctypes
+
+        rc = TimingEvent._hip.hipEventRecord(self.ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_us(self, end) -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value * 1e3
+
+    def __del__(self):
+        hip = TimingEvent._hip if TimingEvent is not None else None
+        if hip is not None and self.ev:
+            hip.hipEventDestroy(self.ev)
+
+
+# Up to this many steps a timed region is launched directly on the stream behind
+# the spin kernel (every launch then fits in the hardware queue while the GPU
+# spins); longer regions are replayed from a HIP graph, whose fixed cost per
+# replay (about 10-25 us here) is then below 0.1 us per step.
+EAGER_MAX_STEPS = 256
+
+
+class Timer:
+    """Times regions of exactly K steps: K launches between two timing events,
+    bracketed by device synchronisations, returning microseconds per step."""
+
+    def __init__(self, step, first: int, steps: int, n_sets: int, launch: str, head: Head):
+        self.step, self.first, self.steps, self.head = step, first, steps, head
+        self.mode = launch
+        if launch == "graph" and steps <= EAGER_MAX_STEPS and head.cycles_per_us > 0:
+            self.mode = "eager+head"
+        self.graphs = capture(step, first, steps, n_sets) if self.mode == "graph" else []
+        self.n_regions = max(1, min(16, math.ceil(n_sets / steps)))
+        # host time to enqueue one step, for sizing the spin ahead of an eager region
+        import torch
+
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(min(steps, 32)):
+            step(first + i)
+        self.host_us = (time.perf_counter() - t0) * 1e6 / min(steps, 32)
+        torch.cuda.synchronize()
+
+    def region(self, r: int) -> float:
+        import torch
+
+        stream = torch.cuda.current_stream()
+        start, end = TimingEvent(), TimingEvent()
+        torch.cuda.synchronize()
+        if self.mode == "graph":
+            self.head(200.0)
+            start.record(stream)
+            self.graphs[r % len(self.graphs)].replay()
+        else:
+            base = self.first + (r % self.n_regions) * self.steps
+            if self.mode == "eager+head":
+                self.head(100.0 + 2.0 * self.steps * self.host_us)
+            start.record(stream)
+            for i in range(self.steps):
+                self.step(base + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_us(end) / self.steps
+
+
+def capture(step, first: int, steps: int, n_sets: int):
+    """Graphs of ``steps`` consecutive steps each, starting at step ``first``, as
+    many as it takes for the replays to cycle through all ``n_sets`` buffer sets."""
+    import torch
+
+    graphs = []
+    n_graphs = max(1, min(16, math.ceil(n_sets / steps)))
+    for j in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(first + j * steps + i)
+        graphs.append(g)
+    for g in graphs:  # one untimed replay each: graph upload
+        g.replay()
+    torch.cuda.synchronize()
+    return graphs
+
+
+def quantiles(v):
+    import numpy as np
+
+    a = np.asarray(v, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "median": float(np.median(a)), "p90": float(np.percentile(a, 90))}
+
+
+class CopyControl:
+    """The library's measurement-control copy of ``nbytes`` bytes per call (half
+    the call's bytes read, half written), over a rotation of source/destination
+    pairs as large as the workload's."""
+
+    def __init__(self, nbytes: int, rotate_bytes: float, dev):
+        import torch
+
+        self.half = max(16, (nbytes // 2) // 16 * 16)
+        self.n_sets = min(128, max(1, int(math.ceil(rotate_bytes / (2 * self.half)))))
+        self.src = [torch.ones(self.half, dtype=torch.uint8, device=dev) for _ in range(self.n_sets)]
+        self.dst = [torch.empty(self.half, dtype=torch.uint8, device=dev) for _ in range(self.n_sets)]
+        self.bytes_per_call = 2 * self.half
+
+    def step(self, i: int):
+        import depthwise_causal_conv1d_amd as dc
+
+        k = i % self.n_sets
+        dc.stream_copy(self.dst[k], self.src[k])
+
+
+def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str, replays: int, head=None,
+            copy: bool = False):
+    """Times the workload (and, with ``copy``, the copy control of the same bytes,
+    interleaved replay by replay)."""
     import torch
     import depthwise_causal_conv1d_amd as dc
     from depthwise_causal_conv1d_amd import workloads as wl
@@ -211,82 +393,141 @@ def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str):
         wk.step(i)
     kernel = dc.dcconv_last_kernel()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    if launch == "graph":
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                wk.step(warmup + i)
-        g.replay()  # one untimed replay: graph upload
-        torch.cuda.synchronize()
+    if head is None:
+        head = Head()
+    cc = None
+    if copy:
+        cc = CopyControl(wk.bytes_per_call, rotate_mb * 2 ** 20, dev)
+        for i in range(warmup):
+            cc.step(i)
+    times, copy_times, t_wall = [], [], 0.0
+    timer = Timer(wk.step, warmup, steps, wk.n_sets, launch, head)
+    ctimer = Timer(cc.step, warmup, steps, cc.n_sets, launch, head) if cc is not None else None
+    for r in range(replays):
         t0 = time.perf_counter()
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record(stream)
-        for i in range(steps):
-            wk.step(warmup + i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / steps
-    res = dict(workload=spec.name, kernel=kernel, ms_per_step=ms, us_per_call=ms * 1e3,
-               wall_ms_per_step=wall * 1e3 / steps, bytes_per_call=wk.bytes_per_call,
+        times.append(timer.region(r))
+        t_wall += time.perf_counter() - t0
+        if ctimer is not None:
+            copy_times.append(ctimer.region(r))
+    del timer, ctimer
+    q = quantiles(times)
+    us = q["median"]
+    ms = us * 1e-3
+    res = dict(workload=spec.name, kernel=kernel, ms_per_step=ms, us_per_call=us,
+               us_p10=q["p10"], us_p90=q["p90"], replays=len(times),
+               wall_ms_per_step=t_wall * 1e3 / (steps * len(times)), bytes_per_call=wk.bytes_per_call,
                gbs=wk.bytes_per_call / (ms * 1e-3) / 1e9,
                rows_per_s=getattr(wk, "rows", spec.N * wk.tokens) / (ms * 1e-3),
                tokens_per_call=wk.tokens,
                buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
+    res["timing_mode"] = "eager+head" if (launch == "graph" and steps <= EAGER_MAX_STEPS
+                                          and head.cycles_per_us > 0) else launch
     res["frac"] = res["gbs"] / PEAK_HBM_GBS
     if getattr(wk, "active", spec.N) != spec.N:
         res["active_rows_per_s"] = wk.active * wk.tokens / (ms * 1e-3)
+    if copy_times:
+        cq = quantiles(copy_times)
+        res["copy"] = {"bytes_per_call": cc.bytes_per_call, "us_per_call": cq["median"], "us_p10": cq["p10"],
+                       "us_p90": cq["p90"], "gbs": cc.bytes_per_call / (cq["median"] * 1e-6) / 1e9,
+                       "buffer_sets": cc.n_sets}
+        res["copy"]["frac"] = res["copy"]["gbs"] / PEAK_HBM_GBS
+        # the update's rate as a fraction of the copy's (same bytes per call)
+        res["frac_of_copy"] = (wk.bytes_per_call / us) / (cc.bytes_per_call / cq["median"])
+        del cc
     host = wk.host
     del wk
     torch.cuda.empty_cache()
     return res, host
 
 
-def cpu_baseline(spec, host, seconds: float):
-    """The oracle as it stands (single thread, plain C) on the same workload."""
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _oracle_rows(spec, host, st, a: int, b: int):
+    """The oracle's update of rows [a, b) of a decode workload, in place on the
+    host state ``st`` (rows of a batch touch distinct slots, so disjoint row
+    ranges may run concurrently)."""
     import numpy as np
     import oracle
+    from depthwise_causal_conv1d_amd import workloads as wl
+
+    tokens = spec.T if spec.one_call else 1
+    strides = wl.state_strides(spec)
+    n, ld = b - a, spec.ld
+    flat = st.reshape(-1)
+    if host["indices"] is None:
+        # row r uses slot r: hand over the state from slot a on
+        sbuf, S, idx = flat[a * strides[0]:], spec.S - a, None
+    else:
+        sbuf, S, idx = flat, spec.S, np.ascontiguousarray(host["indices"][a:b])
+    xs = host["x"].reshape(-1)  # [T, N, ld]
+    if spec.ring:
+        sl = np.ascontiguousarray(host["seqlens"][a:b])
+        for t in range(tokens):  # a multi-token ring call is its tokens' ring steps in order
+            xt = host["x"][t].reshape(-1)[a * ld:]
+            oracle.update_ring(xt, n, spec.D, ld, sbuf, S, spec.L, strides, host["weight"], host["bias"], idx,
+                               sl + t, spec.act)
+    elif tokens == 1:
+        oracle.update_strided(xs[a * ld:], n, spec.D, ld, sbuf, S, spec.L, strides, host["weight"], host["bias"],
+                              idx, spec.act)
+    else:
+        oracle.update_tokens(xs[a * ld:], n, spec.D, tokens, (ld, 1, spec.N * ld), sbuf, S, spec.L, strides,
+                             host["weight"], host["bias"], idx, spec.act)
+
+
+def cpu_baseline(spec, host, seconds: float):
+    """The oracle as it stands (plain C, one thread per call) on the same workload:
+    once on one core, and once on every core of the host (the batch's rows split
+    into one contiguous range per core, each range one oracle call on its own
+    thread; ctypes releases the interpreter lock during the call)."""
+    import concurrent.futures as cf
+    import numpy as np
     from depthwise_causal_conv1d_amd import workloads as wl
 
     if isinstance(spec, wl.PrefillSpec):
         return cpu_baseline_prefill(spec, host, seconds)
     tokens = spec.T if spec.one_call else 1
-    x = np.ascontiguousarray(host["x"][0]) if tokens == 1 else np.ascontiguousarray(host["x"])
-    reps, t_total = 0, 0.0
-    while reps < 2 or t_total < seconds:
-        st = host["state"].copy()
-        t0 = time.perf_counter()
-        if spec.ring:
-            for t in range(tokens):  # a multi-token ring call is its tokens' ring steps in order
-                xt = np.ascontiguousarray(host["x"][t])
-                oracle.update_ring(xt, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
-                                   host["weight"], host["bias"], host["indices"], host["seqlens"] + t, spec.act)
-        elif tokens == 1:
-            oracle.update_strided(x, spec.N, spec.D, spec.ld, st, spec.S, spec.L, wl.state_strides(spec),
-                                  host["weight"], host["bias"], host["indices"], spec.act)
-        else:
-            oracle.update_tokens(x, spec.N, spec.D, tokens, (spec.ld, 1, spec.N * spec.ld), st, spec.S, spec.L,
-                                 wl.state_strides(spec), host["weight"], host["bias"], host["indices"], spec.act)
-        t_total += time.perf_counter() - t0
-        reps += 1
     active = spec.N if host["indices"] is None else int((host["indices"] >= 0).sum())
     b = wl.algorithmic_bytes(spec.N, spec.D, spec.W, spec.L, active, host["bias"] is not None,
                              host["indices"] is not None, spec.layout, tokens, spec.ring)
-    per_call = t_total / reps
-    return {"value": b / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}, {tokens} token(s)) "
-                      f"on host arrays, single thread, {per_call * 1e3:.1f} ms per call",
-            "rows_per_s": spec.N * tokens / per_call}
+
+    def timed(cores: int, budget: float):
+        bounds = [round(i * spec.N / cores) for i in range(cores + 1)]
+        ranges = [(bounds[i], bounds[i + 1]) for i in range(cores) if bounds[i + 1] > bounds[i]]
+        per, total = [], 0.0
+        with cf.ThreadPoolExecutor(max_workers=len(ranges)) as pool:
+            while len(per) < 5 or total < budget:
+                st = host["state"].copy()
+                t0 = time.perf_counter()
+                if len(ranges) == 1:
+                    _oracle_rows(spec, host, st, 0, spec.N)
+                else:
+                    for f in [pool.submit(_oracle_rows, spec, host, st, lo, hi) for lo, hi in ranges]:
+                        f.result()
+                dt = time.perf_counter() - t0
+                per.append(dt)
+                total += dt
+        return float(np.median(per)), len(per), len(ranges)
+
+    one, reps1, _ = timed(1, seconds)
+    cores = host_cores()
+    many, reps_n, threads = timed(cores, seconds / 2)
+    cpu = ""
+    try:
+        cpu = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:
+        pass
+    return {"value": b / many / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps_n} full {spec.name} calls (N={spec.N}, D={spec.D}, L={spec.L}, {tokens} token(s)) "
+                      f"on host arrays, rows split over {threads} threads, median {many * 1e3:.2f} ms per call",
+            "rows_per_s": spec.N * tokens / many, "cpu_model": cpu,
+            "single_thread": {"value": b / one / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": f"{reps1} full calls on one thread, median {one * 1e3:.1f} ms per call",
+                              "rows_per_s": spec.N * tokens / one}}
 
 
 def cpu_baseline_prefill(spec, host, seconds: float):
@@ -335,7 +576,7 @@ def config_of(spec, res, launch):
     cfg["activation"] = cfg.pop("act", None) or "identity"
     cfg["accumulate"] = "f32"
     cfg["buffer_sets"] = res["buffer_sets"]
-    cfg["launch"] = "hipgraph" if launch == "graph" else "eager"
+    cfg["launch"] = res.get("timing_mode", launch)
     return cfg
 
 
@@ -381,28 +622,17 @@ def environment():
     return env
 
 
-def launch_floor(steps: int = 1000) -> float:
-    """Time per launch of a minimal kernel (a 4-byte fill) replayed from one HIP
-    graph, the same way the workload is timed: the per-call cost no kernel can go
-    below on this system, which bounds the measured fraction of peak."""
+def launch_floor(steps: int, replays: int, launch: str, head) -> dict:
+    """Time per launch of a minimal kernel (a 4-byte fill), timed exactly as the
+    workload is: the per-call cost no kernel can go below on this system, which
+    bounds the measured fraction of peak."""
     import torch
     buf = torch.zeros(1, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
     for _ in range(10):
         buf.fill_(0)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(steps):
-            buf.fill_(0)
-    g.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    g.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps * 1e3
+    timer = Timer(lambda i: buf.fill_(0), 0, steps, 1, launch, head)
+    return quantiles([timer.region(r) for r in range(replays)])
 
 
 def copy_calibration(mb: float):
@@ -425,6 +655,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--replays", type=int, default=0,
+                    help="timed replays of the K-step graph (default: enough for 2000 timed steps, at least 5)")
     ap.add_argument("--workload", default="large_decode")
     ap.add_argument("--rotate-mb", type=float, default=1024.0,
                     help="total size of the buffer sets cycled through (beats the 256 MB Infinity Cache)")
@@ -432,6 +664,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--no-copy-control", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
     args = ap.parse_args()
 
@@ -440,6 +673,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the decode "
               "update needs no communication, and a multi-GPU deployment runs one process per GPU on its "
               "own share of the channels.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -454,39 +690,54 @@ def main():
         copy_calibration(args.copy_calibration_mb)
         return
 
+    replays = args.replays if args.replays > 0 else min(200, max(5, math.ceil(2000 / args.steps)))
+    other_replays = max(5, replays // 2)
+    head = Head()
+    copy = not args.no_copy_control
     spec = wl.BY_NAME[args.workload]
-    res, host = measure(spec, args.steps, args.warmup, args.rotate_mb, args.launch)
-    log(f"[bench] {spec.name}: {res['us_per_call']:.3f} us/call, {res['gbs']:.1f} GB/s "
+    res, host = measure(spec, args.steps, args.warmup, args.rotate_mb, args.launch, replays, head, copy)
+    log(f"[bench] {spec.name}: {res['us_per_call']:.3f} us/call (p10 {res['us_p10']:.3f}, p90 {res['us_p90']:.3f}, "
+        f"{res['replays']} replays of {args.steps} steps), {res['gbs']:.1f} GB/s "
         f"({100 * res['frac']:.1f}% of 8 TB/s), {res['rows_per_s'] / 1e6:.2f} M rows/s, kernel {res['kernel']}, "
-        f"{res['buffer_sets']} buffer sets, wall {res['wall_ms_per_step'] * 1e3:.3f} us/step")
+        f"{res['buffer_sets']} buffer sets, timed {res['timing_mode']}")
+    if "copy" in res:
+        log(f"[bench] copy control ({res['copy']['bytes_per_call']} B): {res['copy']['us_per_call']:.3f} us/call "
+            f"({100 * res['copy']['frac']:.1f}% of 8 TB/s); update at {100 * res['frac_of_copy']:.1f}% of the copy")
     others = []
     if not args.no_other_workloads:
         for other in wl.DECODE_WORKLOADS + wl.EXTRA + wl.PREFILL:
             if other.name == spec.name:
                 continue
-            # as many steps as the main workload (a replay of a few hundred steps still
-            # carries a fixed start-up cost of about 0.25 ms), fewer for ~0.1 ms prefill calls
+            # ~0.1 ms prefill calls: fewer steps per replay
             if isinstance(other, wl.PrefillSpec):
-                r, _ = measure(other, max(100, args.steps // 5), 5, args.rotate_mb, args.launch)
+                r, _ = measure(other, max(20, args.steps // 5), 5, args.rotate_mb, args.launch, other_replays,
+                               head, copy)
             else:
-                r, _ = measure(other, args.steps, args.warmup, args.rotate_mb, args.launch)
-            log(f"[bench] {other.name}: {r['us_per_call']:.3f} us/call, {r['gbs']:.1f} GB/s, "
-                f"{r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}")
+                r, _ = measure(other, args.steps, args.warmup, args.rotate_mb, args.launch, other_replays, head,
+                               copy)
+            log(f"[bench] {other.name}: {r['us_per_call']:.3f} us/call (p10 {r['us_p10']:.3f}, p90 "
+                f"{r['us_p90']:.3f}), {r['gbs']:.1f} GB/s, {r['rows_per_s'] / 1e6:.2f} M rows/s, kernel {r['kernel']}"
+                + (f"; copy {r['copy']['us_per_call']:.3f} us, {100 * r['frac_of_copy']:.1f}% of it"
+                   if "copy" in r else ""))
             entry = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
-                     if k in ("workload", "kernel", "us_per_call", "gbs", "frac", "rows_per_s",
-                              "active_rows_per_s", "bytes_per_call", "tokens_per_call")}
+                     if k in ("workload", "kernel", "us_per_call", "us_p10", "us_p90", "gbs", "frac", "rows_per_s",
+                              "active_rows_per_s", "bytes_per_call", "tokens_per_call", "frac_of_copy")}
+            if "copy" in r:
+                entry["copy_us"] = round(r["copy"]["us_per_call"], 4)
             entry["traffic"] = read_traffic(r["kernel"], other.name)
             others.append(entry)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, host, args.cpu_seconds)
-        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads ({cpu['sample']}); "
+            f"one thread {cpu.get('single_thread', {}).get('value', float('nan')):.3f} GB/s")
 
     # the same calls on one buffer set, resident in the 256 MB Infinity Cache: a
     # cache figure, reported beside the HBM one and never as a fraction of HBM peak
-    warm, _ = measure(spec, args.steps, args.warmup, 0.0, args.launch)
+    warm, _ = measure(spec, args.steps, args.warmup, 0.0, args.launch, other_replays, head)
     log(f"[bench] {spec.name} warm (one buffer set, Infinity Cache resident): {warm['us_per_call']:.3f} us/call")
-    floor_us = launch_floor()
+    floor = launch_floor(args.steps, other_replays, args.launch, head)
+    floor_us = floor["median"]
     # under a profiler every launch carries the tracer's own cost, so the floor can
     # reach the call's period; the split is then meaningless
     rest_us = res["us_per_call"] - floor_us
@@ -514,6 +765,15 @@ def main():
         "kernel": res["kernel"],
         "roofline": {"bound": "hbm", "achieved": round(res["gbs"], 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(res["frac"], 4), "traffic": traffic},
+        # every timed region is exactly `steps` steps; ms_per_step is the median over regions
+        "timing": {"regions": res["replays"], "steps_per_region": args.steps, "mode": res["timing_mode"],
+                   "events": "hipEventDisableSystemFence",
+                   "us_per_call": {"p10": round(res["us_p10"], 4), "median": round(res["us_per_call"], 4),
+                                   "p90": round(res["us_p90"], 4)}},
+        # the same byte count moved by a plain copy, interleaved with the update replay by replay
+        "copy_control": None if "copy" not in res else {
+            **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["copy"].items()},
+            "frac_of_copy": round(res["frac_of_copy"], 4)},
         # per-call floor of a graph-replayed launch, measured beside the workload: a call of
         # B bytes cannot exceed B / (B / peak + floor), the ceiling the fraction is read against
         "launch_floor_us": round(floor_us, 3),

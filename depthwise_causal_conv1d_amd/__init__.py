@@ -29,7 +29,7 @@ __all__ = [
     "dcconv_abi_version", "dcconv_last_error", "dcconv_last_kernel", "dcconv_update",
     "dcconv_update_tokens", "causal_conv1d_update", "causal_conv1d_update_out",
     "causal_conv1d_update_tokens", "dcconv_prefill", "causal_conv1d", "library_path", "DcconvError",
-    "DCCONV_DEV_BAD_SEQ", "DCCONV_DEV_BAD_SEQLEN",
+    "DCCONV_DEV_BAD_SEQ", "DCCONV_DEV_BAD_SEQLEN", "dcconv_stream_copy", "stream_copy",
 ]
 
 DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED, DCCONV_EHIP = 0, 1, 2, 3
@@ -94,6 +94,8 @@ def _load() -> ctypes.CDLL:
                                            vp, i64, vp, i32,                 # weight, w, bias, activation
                                            vp, i64, i64, i64,                # out, os_n, os_d, os_t
                                            vp, vp]                           # dev_status, stream
+            lib.dcconv_stream_copy.restype = i32
+            lib.dcconv_stream_copy.argtypes = [vp, vp, i64, vp]      # dst, src, bytes, stream
             _lib = lib
     return _lib
 
@@ -149,6 +151,11 @@ def dcconv_prefill(x, n, d, t, xs_n, xs_d, xs_t, seq_starts, conv_state, s, l, s
     return _load().dcconv_prefill(x, n, d, t, xs_n, xs_d, xs_t, seq_starts, conv_state, s, l, st_s, st_d, st_l,
                                   conv_state_indices, has_initial_state, weight, w, bias, activation, out, os_n,
                                   os_d, os_t, dev_status, stream)
+
+
+def dcconv_stream_copy(dst, src, nbytes, stream) -> int:
+    """The measurement-control copy, one to one (pointers as ints)."""
+    return _load().dcconv_stream_copy(dst, src, nbytes, stream)
 
 
 # ------------------------------------------------------------ tensor front end
@@ -369,3 +376,20 @@ def causal_conv1d(x, weight, bias=None, activation=None, *, conv_state=None, con
                             _ptr(dev_status), stream)
     _raise_for(rc)
     return (out, state_out) if state_out is not None else out
+
+
+def stream_copy(dst, src) -> None:
+    """Copy the bytes of ``src`` into ``dst`` (two contiguous device tensors of the
+    same byte size) on the current stream, with the update kernels' access
+    pattern: the bandwidth control a benchmark times beside the update."""
+    import torch
+
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("stream_copy needs contiguous tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or dst.device != src.device:
+        raise ValueError("stream_copy needs two tensors of one size on one device")
+    with torch.cuda.device(src.device):
+        rc = dcconv_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes,
+                                torch.cuda.current_stream(src.device).cuda_stream)
+    _raise_for(rc)

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdcconv.so")
-SOURCES = ["abi.hip", "update.hip", "update_tokens.hip", "prefill.hip", "update_ring.hip"]
+SOURCES = ["abi.hip", "update.hip", "update_tokens.hip", "prefill.hip", "update_ring.hip", "copy_control.hip"]
 ARCH = "gfx950"
 
 

@@ -392,3 +392,17 @@ extern "C" int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
     if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
     return succeed(name);
 }
+
+extern "C" int dcconv_stream_copy(void *dst, const void *src, int64_t bytes, void *stream) {
+    if (bytes < 0) return fail(DCCONV_EINVAL, "bytes=%lld is negative", (long long)bytes);
+    if (bytes == 0) return succeed("");
+    if (dst == nullptr || src == nullptr) return fail(DCCONV_EINVAL, "dst and src must not be NULL");
+    if (bytes % 16 != 0) return fail(DCCONV_EINVAL, "bytes=%lld is not a multiple of 16", (long long)bytes);
+    if (bytes > ((int64_t)1 << 47)) return fail(DCCONV_EINVAL, "bytes=%lld exceeds 2^47", (long long)bytes);
+    if (!aligned(dst, 16) || !aligned(src, 16)) return fail(DCCONV_EINVAL, "dst and src must be 16-byte aligned");
+    if (overlaps(span("dst", dst, bytes), span("src", src, bytes)))
+        return fail(DCCONV_EINVAL, "dst and src overlap");
+    const hipError_t err = dcconv::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return succeed("stream_copy_v8");
+}

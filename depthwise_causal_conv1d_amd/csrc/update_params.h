@@ -78,4 +78,7 @@ hipError_t launch_update_tokens_ring(const TokensParams &p, StateLayout layout, 
 hipError_t launch_prefill(const PrefillParams &p, StateLayout layout, int activation, hipStream_t stream,
                           const char **kernel_name);
 
+// The measurement control behind dcconv_stream_copy (validated on the host).
+hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
+
 }  // namespace dcconv

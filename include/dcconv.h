@@ -247,6 +247,26 @@ int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
                    int32_t *dev_status,
                    void *stream);
 
+/*
+ * dcconv_stream_copy -- measurement control, not part of the operation.
+ * The page "Composing multi-kernel blocks in Python" (section "Measuring a block
+ * honestly") asks for a plain baseline timed in the same run as the block it
+ * judges.  This copies `bytes` bytes from src to dst with the access pattern of
+ * the update kernels (coalesced 16-byte non-temporal loads and stores, about
+ * 2048 wavefronts for 16 MiB), so a benchmark can time what moving the update's
+ * bytes costs with no arithmetic at all.
+ *
+ * dst, src  device pointers, 16-byte aligned, not overlapping.  The caller owns
+ *           both; dst is written, src only read.
+ * bytes     a multiple of 16, 0 <= bytes <= 2^47.  0 returns DCCONV_OK and
+ *           enqueues nothing.
+ * stream    hipStream_t (NULL = the null stream); asynchronous like every call.
+ *
+ * Returns DCCONV_OK, DCCONV_EINVAL (negative, unaligned or overlapping
+ * arguments, or a size not a multiple of 16) or DCCONV_EHIP.
+ */
+int dcconv_stream_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

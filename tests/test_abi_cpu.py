@@ -324,3 +324,19 @@ def test_prefill_frontend_checks():
         dc.causal_conv1d(x, w)
     with pytest.raises(NotImplementedError, match="inference only"):
         dc.causal_conv1d(x.clone().float().requires_grad_(), w)
+
+
+def test_stream_copy_refusals_before_any_hip_call():
+    # the measurement-control copy validates on the host; fake addresses never
+    # reach the device because every case here is refused (or empty)
+    a, b = 0x7F0000000000, 0x7F0000100000
+    assert dc.dcconv_stream_copy(a, b, 24, None) == dc.DCCONV_EINVAL
+    assert "multiple of 16" in dc.dcconv_last_error()
+    assert dc.dcconv_stream_copy(a + 8, b, 16, None) == dc.DCCONV_EINVAL
+    assert "aligned" in dc.dcconv_last_error()
+    assert dc.dcconv_stream_copy(a + 16, a, 32, None) == dc.DCCONV_EINVAL
+    assert "overlap" in dc.dcconv_last_error()
+    assert dc.dcconv_stream_copy(a, b, -16, None) == dc.DCCONV_EINVAL
+    assert dc.dcconv_stream_copy(0, b, 16, None) == dc.DCCONV_EINVAL
+    assert dc.dcconv_stream_copy(a, b, 0, None) == dc.DCCONV_OK
+    assert dc.dcconv_last_kernel() == ""

@@ -72,8 +72,37 @@ def test_bench_refuses_several_gpus():
 def test_cpu_baseline_leg(name):
     spec = wl.BY_NAME[name]
     res = bench.cpu_baseline(spec, wl.make(spec), seconds=0.0)
-    assert res["kind"] == "oracle" and res["cores"] == 1 and res["unit"] == "GB/s" and res["value"] > 0
+    assert res["kind"] == "oracle" and res["cores"] >= 1 and res["unit"] == "GB/s" and res["value"] > 0
+    one = res["single_thread"]
+    assert one["cores"] == 1 and one["value"] > 0
     json.dumps(res)
+
+
+_SPLIT_CASES = [
+    wl.Spec("split_plain", N=13, D=64, W=4, L=3, S=15, ld=72, bias=False, act="silu", routing="none", seed=7),
+    wl.Spec("split_padded", N=16, D=40, W=4, L=4, S=64, ld=40, bias=True, act=None, routing="padded", n_unique=11,
+            seed=8),
+    wl.Spec("split_tokens", N=9, D=32, W=4, L=5, S=20, ld=32, bias=True, act="silu", routing="unique", T=6,
+            seed=9, one_call=True),
+    wl.Spec("split_ring", N=10, D=48, W=4, L=3, S=10, ld=48, bias=False, act="silu", routing="none",
+            layout="channel_last", ring=True, T=3, one_call=True, seed=10),
+    wl.Spec("split_channel_last", N=7, D=24, W=4, L=6, S=9, ld=24, bias=True, act=None, routing="none",
+            layout="channel_last", seed=11),
+]
+
+
+@pytest.mark.parametrize("spec", _SPLIT_CASES, ids=lambda s: s.name)
+def test_cpu_baseline_row_split_matches_one_call(spec):
+    # the all-cores leg runs disjoint row ranges as separate oracle calls; the
+    # state they leave must be the one a single whole-batch call leaves
+    host = wl.make(spec)
+    whole = host["state"].copy()
+    bench._oracle_rows(spec, host, whole, 0, spec.N)
+    split = host["state"].copy()
+    for a, b in ((0, 3), (3, 4), (4, spec.N)):
+        bench._oracle_rows(spec, host, split, a, b)
+    assert np.array_equal(whole, split)
+    assert not np.array_equal(whole, host["state"])
 
 
 def test_prefill_bytes_by_hand():
