@@ -19,6 +19,9 @@ constexpr int64_t kMaxBlocks = 1 << 20;         // grid cap: min(units, kMaxBloc
 // Two rows per wave once the grid still has this many waves: fewer, fuller waves
 // keep more bytes in flight per wave and share one weight load between rows.
 constexpr int64_t kMinWavesForTwoRows = 1024;
+// The one-token update spreads a batch over 128-channel waves (the narrow form)
+// when its 512-channel grid, rows x tiles, holds at most this many waves.
+constexpr int64_t kNarrowMaxWaves = 512;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -44,6 +47,47 @@ __device__ __forceinline__ u32x4 buffer_load(Buffer b, uint32_t offset) {
 template <int POLICY>
 __device__ __forceinline__ void buffer_store(u32x4 v, Buffer b, uint32_t offset) {
     __builtin_amdgcn_raw_buffer_store_b128(v, b, offset, 0, POLICY);
+}
+
+// NW consecutive 32-bit words at byte `offset` of a buffer, moved with the widest
+// accesses that fit (16, 12, 8 or 4 bytes), so a lane's run of 4*NW bytes is
+// one access when NW <= 4.
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int NW, int POLICY>
+__device__ __forceinline__ void buffer_load_words(Buffer b, uint32_t offset, uint32_t (&w)[NW]) {
+#pragma unroll
+    for (int i = 0; i < NW; i += 4) {
+        const uint32_t at = offset + 4u * (uint32_t)i;
+        if (NW - i >= 4) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b, at, 0, POLICY);
+            w[i] = v[0], w[i + 1] = v[1], w[i + 2] = v[2], w[i + 3] = v[3];
+        } else if (NW - i == 3) {
+            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(b, at, 0, POLICY);
+            w[i] = v[0], w[i + 1] = v[1], w[i + 2] = v[2];
+        } else if (NW - i == 2) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(b, at, 0, POLICY);
+            w[i] = v[0], w[i + 1] = v[1];
+        } else {
+            w[i] = __builtin_amdgcn_raw_buffer_load_b32(b, at, 0, POLICY);
+        }
+    }
+}
+template <int NW, int POLICY>
+__device__ __forceinline__ void buffer_store_words(const uint32_t (&w)[NW], Buffer b, uint32_t offset) {
+#pragma unroll
+    for (int i = 0; i < NW; i += 4) {
+        const uint32_t at = offset + 4u * (uint32_t)i;
+        if (NW - i >= 4) {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]}, b, at, 0, POLICY);
+        } else if (NW - i == 3) {
+            __builtin_amdgcn_raw_buffer_store_b96(u32x3{w[i], w[i + 1], w[i + 2]}, b, at, 0, POLICY);
+        } else if (NW - i == 2) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[i], w[i + 1]}, b, at, 0, POLICY);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(w[i], b, at, 0, POLICY);
+        }
+    }
 }
 
 // BF16 held in the low / high half of a 32-bit word, as FP32 (exact).

@@ -45,17 +45,17 @@
 namespace dcconv {
 namespace {
 
-// The arithmetic for the 8 channels a lane owns.
-//   hist[4L]: the old state of the 8 channels, channel-major (oldest first)
-//   xw[4]:    x of the 8 channels;  wf[32]: weights [8][4] as FP32;  bf[8]: bias
-// Produces the 8 outputs (packed BF16) and the new state (same order as hist).
-template <int L, int ACT>
-__device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uint32_t (&xw)[4],
-                                        const float (&wf)[32], const float (&bf)[8], bool has_bias,
-                                        uint32_t (&outw)[4], uint32_t (&nhist)[4 * L]) {
-    float y[kChPerLane];
+// The arithmetic for the C channels a lane owns (C even).
+//   hist[C*L/2]: the old state of the C channels, channel-major (oldest first)
+//   xw[C/2]:     x of the C channels;  wf[4C]: weights [C][4] as FP32;  bf[C]: bias
+// Produces the C outputs (packed BF16) and the new state (same order as hist).
+template <int L, int ACT, int C>
+__device__ __forceinline__ void update_lane(const uint32_t (&hist)[C * L / 2], const uint32_t (&xw)[C / 2],
+                                            const float (&wf)[4 * C], const float (&bf)[C], bool has_bias,
+                                            uint32_t (&outw)[C / 2], uint32_t (&nhist)[C * L / 2]) {
+    float y[C];
 #pragma unroll
-    for (int c = 0; c < kChPerLane; ++c) {
+    for (int c = 0; c < C; ++c) {
         // history[L+1-W+j] for W = 4: the newest three state values, then x.
         // BF16 x BF16 products are exact in FP32, so the fused multiply-adds give
         // the same bits as separate products summed from j = 0 upward.
@@ -67,13 +67,13 @@ __device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uin
         y[c] = activate<ACT>(acc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) outw[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+    for (int i = 0; i < C / 2; ++i) outw[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
     // New state: each channel's history moves one place towards the oldest end
     // and x becomes the newest value.  New element e is x[e / L] when e is the
     // last position of its channel, else old element e + 1.  Each new word (two
     // elements) is one byte permute of the two words its halves come from.
 #pragma unroll
-    for (int i = 0; i < 4 * L; ++i) {
+    for (int i = 0; i < C * L / 2; ++i) {
         uint32_t src[2];
         int half[2];
 #pragma unroll
@@ -87,14 +87,18 @@ __device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uin
                 half[k] = (e + 1) & 1;
             }
         }
-        // v_perm_b32(a, b, sel): selector bytes 0-3 pick bytes of b, 4-7 bytes of a.
-        const uint32_t sel_lo = half[0] ? 0x0302u : 0x0100u;  // from b = src[0]
-        const uint32_t sel_hi = half[1] ? 0x0706u : 0x0504u;  // from a = src[1]
-        nhist[i] = __builtin_amdgcn_perm(src[1], src[0], (sel_hi << 16) | sel_lo);
+        nhist[i] = pick_halves(src[0], half[0], src[1], half[1]);
     }
 }
 
-template <int L, int ACT, int R, bool HAS_BIAS>
+template <int L, int ACT>
+__device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uint32_t (&xw)[4],
+                                        const float (&wf)[32], const float (&bf)[8], bool has_bias,
+                                        uint32_t (&outw)[4], uint32_t (&nhist)[4 * L]) {
+    update_lane<L, ACT, kChPerLane>(hist, xw, wf, bf, has_bias, outw, nhist);
+}
+
+template <int L, int ACT, int R, bool HAS_BIAS, bool INDEXED>
 __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int tiles_per_row,
                                                             int64_t block_units) {
     __shared__ u32x4 stage_all[kWavesPerBlock][R][kWave * L];
@@ -115,41 +119,59 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;  // x / out / bias bytes of the tile
 
-        // Route every row of the group (wave-uniform): slot, -1 = write zeros,
-        // -2 = no such row.
-        int slot[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = group * R + r;
-            // route_row's result is the same in every lane; saying so keeps the
-            // buffer descriptors built from it in scalar registers.
-            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p.idx, p.status, p.n, p.s, row, lane) : -2);
-        }
-
         // Issue every load up front: this wave's share of the weight tile, the
         // bias, then each row's x and state run.  Buffer descriptors bound each
-        // access: a row that must not touch memory gets empty descriptors (its
-        // loads return zeros, its stores are dropped) and the lanes past a ragged
-        // tile's end fall outside the descriptor.  Nothing below branches on the
-        // row, so the compiler can wait for each row's own loads only.
+        // access: a row that must not touch the state gets an empty state
+        // descriptor (its loads return zeros, its stores are dropped), a row
+        // past the batch gets empty x and out descriptors, and the lanes past a
+        // ragged tile's end fall outside every descriptor.  Nothing below
+        // branches on the row, so the compiler can wait for each row's own
+        // loads only.
         __builtin_amdgcn_s_setprio(3);  // get the loads of every wave queued early
         u32x4 wraw[kWeightChunks];
         weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
-        Buffer sbuf[R], obuf[R];
         u32x4 xv[R], sv[R][L];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
+        Buffer sbuf[R], obuf[R];
+        int slot[R];
+        auto load_x = [&](int r) {
+            const int row = min(group * R + r, p.n - 1);
+            xv[r] = buffer_load<kStream>(make_buffer(p.x + (int64_t)row * p.ld + c0, group * R + r < p.n ? vec_bytes : 0u),
+                                         lane_bytes);
+        };
+        // Route a row (wave-uniform): slot, -1 = write zeros, -2 = no such row.
+        // route_row's result is the same in every lane; saying so keeps the
+        // buffer descriptors built from it in scalar registers.
+        auto route = [&](int r) {
+            const int row = group * R + r;
+            slot[r] = __builtin_amdgcn_readfirstlane(
+                row < p.n ? route_row(INDEXED ? p.idx : nullptr, p.status, p.n, p.s, row, lane) : -2);
+        };
+        auto load_state = [&](int r) {
             const bool live = slot[r] >= 0;
             const int row = min(group * R + r, p.n - 1);
-            const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u);
             sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + (int64_t)c0 * L : p.x,
                                   live ? vec_bytes * L : 0u);
             obuf[r] = make_buffer(p.out + (int64_t)row * p.d + c0, slot[r] != -2 ? vec_bytes : 0u);
-            xv[r] = buffer_load<kStream>(xbuf, lane_bytes);
 #pragma unroll
             for (int j = 0; j < L; ++j) sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
+        };
+        if constexpr (!INDEXED) {
+            // row r uses slot r: each row's x and state in row order, so the
+            // first row's data is complete first
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_x(r), route(r), load_state(r);
+        } else {
+            // every x ahead of the index table, whose latency it then shares;
+            // the state runs once their slots are known (x of a padding row is
+            // read but not used)
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_x(r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) route(r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_state(r);
         }
         __builtin_amdgcn_s_setprio(0);
 
@@ -209,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
     } while (bu < block_units);
 }
 
-template <int L, int ACT, int R, bool HAS_BIAS>
+template <int L, int ACT, int R, bool HAS_BIAS, bool INDEXED>
 __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p, int tiles_per_row,
                                                                  int64_t block_units) {
     __shared__ u32x4 weight_tile[4 * kWave];
@@ -235,32 +257,46 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
         // it can neither read nor write a neighbouring plane.
         const uint32_t plane_lane = lane < lanes_used ? lane_bytes : 0x80000000u;
 
-        int slot[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = group * R + r;
-            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p.idx, p.status, p.n, p.s, row, lane) : -2);
-        }
-
+        // Loads in the compact kernel's order: per row without an index table,
+        // every x ahead of the index table with one.
         __builtin_amdgcn_s_setprio(3);
         u32x4 wraw[kWeightChunks];
         weight_tile_issue(wraw, p.weight, c0, vec_bytes, wave, lane_bytes);
         u32x4 bv = u32x4{0u, 0u, 0u, 0u};
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
-        Buffer sbuf[R], obuf[R];
         u32x4 xv[R], pv[R][kRead];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
+        Buffer sbuf[R], obuf[R];
+        int slot[R];
+        auto load_x = [&](int r) {
+            const int row = min(group * R + r, p.n - 1);
+            xv[r] = buffer_load<kStream>(make_buffer(p.x + (int64_t)row * p.ld + c0, group * R + r < p.n ? vec_bytes : 0u),
+                                         lane_bytes);
+        };
+        auto route = [&](int r) {
+            const int row = group * R + r;
+            slot[r] = __builtin_amdgcn_readfirstlane(
+                row < p.n ? route_row(INDEXED ? p.idx : nullptr, p.status, p.n, p.s, row, lane) : -2);
+        };
+        auto load_state = [&](int r) {
             const bool live = slot[r] >= 0;
             const int row = min(group * R + r, p.n - 1);
-            const Buffer xbuf = make_buffer(p.x + (int64_t)row * p.ld + c0, live ? vec_bytes : 0u);
             sbuf[r] = make_buffer(live ? p.state + (int64_t)slot[r] * p.st_s + c0 : p.x,
                                   live ? plane_bytes * (uint32_t)(L - 1) + vec_bytes : 0u);
             obuf[r] = make_buffer(p.out + (int64_t)row * p.d + c0, slot[r] != -2 ? vec_bytes : 0u);
-            xv[r] = buffer_load<kStream>(xbuf, lane_bytes);
 #pragma unroll
             for (int k = 0; k < kRead; ++k)
                 pv[r][k] = buffer_load<kStream>(sbuf[r], plane_bytes * (uint32_t)(kFirst + k) + plane_lane);
+        };
+        if constexpr (!INDEXED) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_x(r), route(r), load_state(r);
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_x(r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) route(r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_state(r);
         }
         __builtin_amdgcn_s_setprio(0);
 
@@ -304,6 +340,99 @@ __global__ __launch_bounds__(kBlock) void update_channel_last_v8(UpdateParams p,
         __syncthreads();  // the weight tile is reused by the next unit
         bu += kMaxBlocks;
     } while (bu < block_units);
+}
+
+// The narrow form, for batches too small to fill the GPU with 512-channel
+// waves (few rows): one wavefront per (row, 128-channel tile), 2 channels per
+// lane, so a row spreads over four times as many waves.  A lane's two channels
+// of compact state are 4L contiguous bytes, so the wave's L*256-byte run moves
+// as one coalesced access per lane (12 bytes at L = 3) and needs no LDS
+// transpose; channel-last planes are one 4-byte access per lane.  Weights (16
+// bytes per lane) are loaded directly, so there is no block barrier either:
+// every wave runs its own short chain (x, weights and bias ahead of the index
+// table, then the state, the arithmetic and all stores).
+constexpr int kNarrowCh = 2;                    // channels per lane
+constexpr int kNarrowTile = kWave * kNarrowCh;  // 128 channels per wave
+
+template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST>
+__global__ __launch_bounds__(kWave) void update_narrow(UpdateParams p, int tiles_per_row, int64_t units) {
+    constexpr int kFirst = (CHANNEL_LAST && L > 3) ? 1 : 0;  // see update_channel_last_v8
+    const int lane = threadIdx.x;
+    const uint32_t lane_word = (uint32_t)lane * 4u;
+    const uint32_t plane_bytes = (uint32_t)p.st_l * 2u;
+    // min(units, kMaxBlocks) blocks: the first unit needs no test (see for_each_unit)
+    int64_t u = blockIdx.x;
+    do {
+        const int row = (int)(u / tiles_per_row);
+        const int c0 = (int)(u - (int64_t)row * tiles_per_row) * kNarrowTile;
+        const int lanes_used = min(kWave, (p.d - c0) / kNarrowCh);
+        const uint32_t word_bytes = (uint32_t)lanes_used * 4u;  // x / out / bias bytes of the tile
+
+        __builtin_amdgcn_s_setprio(3);
+        const u32x4 wv = buffer_load<kCached>(make_buffer(p.weight + (int64_t)c0 * 4, word_bytes * 4u), lane * 16u);
+        uint32_t bw = 0u;
+        if (HAS_BIAS) bw = __builtin_amdgcn_raw_buffer_load_b32(make_buffer(p.bias + c0, word_bytes), lane_word, 0, kCached);
+        const uint32_t xw[1] = {__builtin_amdgcn_raw_buffer_load_b32(
+            make_buffer(p.x + (int64_t)row * p.ld + c0, word_bytes), lane_word, 0, kStream)};
+        const int slot = __builtin_amdgcn_readfirstlane(route_row(p.idx, p.status, p.n, p.s, row, lane));
+        const bool live = slot >= 0;
+        // compact: channel-major words (channel 0's L values, then channel 1's);
+        // channel-last: word k = position k of both channels
+        uint32_t hist[L];
+        Buffer sbuf;
+        uint32_t plane_lane = 0u;
+        if (CHANNEL_LAST) {
+            sbuf = make_buffer(live ? p.state + (int64_t)slot * p.st_s + c0 : p.x,
+                               live ? plane_bytes * (uint32_t)(L - 1) + word_bytes : 0u);
+            plane_lane = lane < lanes_used ? lane_word : 0x80000000u;
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+                hist[k] = k < kFirst ? 0u
+                                     : __builtin_amdgcn_raw_buffer_load_b32(sbuf, plane_bytes * (uint32_t)k + plane_lane,
+                                                                            0, kStream);
+        } else {
+            sbuf = make_buffer(live ? p.state + (int64_t)slot * p.st_s + (int64_t)c0 * L : p.x,
+                               live ? word_bytes * L : 0u);
+            buffer_load_words<L, kStream>(sbuf, lane_word * L, hist);
+        }
+        __builtin_amdgcn_s_setprio(0);
+
+        float wf[4 * kNarrowCh], bf[kNarrowCh];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wf[2 * q] = lo_f32(wv[q]), wf[2 * q + 1] = hi_f32(wv[q]);
+        bf[0] = lo_f32(bw), bf[1] = hi_f32(bw);
+        uint32_t outw[1], nhist[L];
+        if (CHANNEL_LAST) {
+            float y[kNarrowCh];
+#pragma unroll
+            for (int c = 0; c < kNarrowCh; ++c) {
+                float acc = half_f32(hist[L - 3], c) * wf[4 * c + 0];
+                acc = __builtin_fmaf(half_f32(hist[L - 2], c), wf[4 * c + 1], acc);
+                acc = __builtin_fmaf(half_f32(hist[L - 1], c), wf[4 * c + 2], acc);
+                acc = __builtin_fmaf(half_f32(xw[0], c), wf[4 * c + 3], acc);
+                if (HAS_BIAS) acc += bf[c];
+                y[c] = activate<ACT>(acc);
+            }
+            outw[0] = pack_bf16x2(y[0], y[1]);
+#pragma unroll
+            for (int k = 0; k < L - 1; ++k) nhist[k] = hist[k + 1];
+            nhist[L - 1] = xw[0];
+        } else {
+            update_lane<L, ACT, kNarrowCh>(hist, xw, wf, bf, HAS_BIAS, outw, nhist);
+        }
+        // all stores last; a padding row writes zeros and no state
+        __builtin_amdgcn_sched_barrier(0);
+        if (CHANNEL_LAST) {
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+                __builtin_amdgcn_raw_buffer_store_b32(nhist[k], sbuf, plane_bytes * (uint32_t)k + plane_lane, 0, kStream);
+        } else {
+            buffer_store_words<L, kStream>(nhist, sbuf, lane_word * L);
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(live ? outw[0] : 0u, make_buffer(p.out + (int64_t)row * p.d + c0, word_bytes),
+                                              lane_word, 0, kStream);
+        u += kMaxBlocks;
+    } while (u < units);
 }
 
 template <int ACT>
@@ -354,16 +483,21 @@ hipError_t launch_compact_l(const UpdateParams &p, int tiles, hipStream_t stream
                             const char *name_one_row, const char *name_two_rows) {
     const bool bias = p.bias != nullptr;
     const int64_t groups_two = (p.n + 1) / 2;
+    const bool indexed = p.idx != nullptr;
     if (two_rows_per_wave(p.n, tiles)) {
         *name = name_two_rows;
         const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
-        return bias ? launch(update_compact_v8<L, ACT, 2, true>, p, tiles, block_units, kBlock, stream)
-                    : launch(update_compact_v8<L, ACT, 2, false>, p, tiles, block_units, kBlock, stream);
+        return bias ? (indexed ? launch(update_compact_v8<L, ACT, 2, true, true>, p, tiles, block_units, kBlock, stream)
+                               : launch(update_compact_v8<L, ACT, 2, true, false>, p, tiles, block_units, kBlock, stream))
+                    : (indexed ? launch(update_compact_v8<L, ACT, 2, false, true>, p, tiles, block_units, kBlock, stream)
+                               : launch(update_compact_v8<L, ACT, 2, false, false>, p, tiles, block_units, kBlock, stream));
     }
     *name = name_one_row;
     const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
-    return bias ? launch(update_compact_v8<L, ACT, 1, true>, p, tiles, block_units, kBlock, stream)
-                : launch(update_compact_v8<L, ACT, 1, false>, p, tiles, block_units, kBlock, stream);
+    return bias ? (indexed ? launch(update_compact_v8<L, ACT, 1, true, true>, p, tiles, block_units, kBlock, stream)
+                           : launch(update_compact_v8<L, ACT, 1, true, false>, p, tiles, block_units, kBlock, stream))
+                : (indexed ? launch(update_compact_v8<L, ACT, 1, false, true>, p, tiles, block_units, kBlock, stream)
+                           : launch(update_compact_v8<L, ACT, 1, false, false>, p, tiles, block_units, kBlock, stream));
 }
 
 template <int ACT>
@@ -400,16 +534,22 @@ hipError_t launch_channel_last_l(const UpdateParams &p, int tiles, hipStream_t s
                                  const char *name_one_row, const char *name_two_rows) {
     const bool bias = p.bias != nullptr;
     const int64_t groups_two = (p.n + 1) / 2;
+    const bool indexed = p.idx != nullptr;
     if (two_rows_per_wave(p.n, tiles)) {
         *name = name_two_rows;
         const int64_t block_units = tiles * ((groups_two + kWavesPerBlock - 1) / kWavesPerBlock);
-        return bias ? launch(update_channel_last_v8<L, ACT, 2, true>, p, tiles, block_units, kBlock, stream)
-                    : launch(update_channel_last_v8<L, ACT, 2, false>, p, tiles, block_units, kBlock, stream);
+        return bias ? (indexed ? launch(update_channel_last_v8<L, ACT, 2, true, true>, p, tiles, block_units, kBlock, stream)
+                               : launch(update_channel_last_v8<L, ACT, 2, true, false>, p, tiles, block_units, kBlock, stream))
+                    : (indexed ? launch(update_channel_last_v8<L, ACT, 2, false, true>, p, tiles, block_units, kBlock, stream)
+                               : launch(update_channel_last_v8<L, ACT, 2, false, false>, p, tiles, block_units, kBlock,
+                                        stream));
     }
     *name = name_one_row;
     const int64_t block_units = tiles * (((int64_t)p.n + kWavesPerBlock - 1) / kWavesPerBlock);
-    return bias ? launch(update_channel_last_v8<L, ACT, 1, true>, p, tiles, block_units, kBlock, stream)
-                : launch(update_channel_last_v8<L, ACT, 1, false>, p, tiles, block_units, kBlock, stream);
+    return bias ? (indexed ? launch(update_channel_last_v8<L, ACT, 1, true, true>, p, tiles, block_units, kBlock, stream)
+                           : launch(update_channel_last_v8<L, ACT, 1, true, false>, p, tiles, block_units, kBlock, stream))
+                : (indexed ? launch(update_channel_last_v8<L, ACT, 1, false, true>, p, tiles, block_units, kBlock, stream)
+                           : launch(update_channel_last_v8<L, ACT, 1, false, false>, p, tiles, block_units, kBlock, stream));
 }
 
 template <int ACT>
@@ -442,6 +582,31 @@ hipError_t launch_channel_last(const UpdateParams &p, int tiles, hipStream_t str
 #undef DCCONV_CL_CASE
 }
 
+template <int ACT, bool CHANNEL_LAST>
+hipError_t launch_narrow(const UpdateParams &p, hipStream_t stream, const char **name) {
+    const int tiles = (p.d + kNarrowTile - 1) / kNarrowTile;
+    const int64_t units = (int64_t)p.n * tiles;
+    const bool bias = p.bias != nullptr;
+#define DCCONV_NARROW_CASE(LL)                                                                                 \
+    case LL:                                                                                                    \
+        *name = CHANNEL_LAST ? (ACT == DCCONV_ACT_SILU ? "update_narrow<L=" #LL ",silu,channel_last>"           \
+                                                       : "update_narrow<L=" #LL ",identity,channel_last>")      \
+                             : (ACT == DCCONV_ACT_SILU ? "update_narrow<L=" #LL ",silu,compact>"                \
+                                                       : "update_narrow<L=" #LL ",identity,compact>");          \
+        return bias ? launch(update_narrow<LL, ACT, true, CHANNEL_LAST>, p, tiles, units, kWave, stream)        \
+                    : launch(update_narrow<LL, ACT, false, CHANNEL_LAST>, p, tiles, units, kWave, stream);
+    switch (p.l) {
+        DCCONV_NARROW_CASE(3)
+        DCCONV_NARROW_CASE(4)
+        DCCONV_NARROW_CASE(5)
+        DCCONV_NARROW_CASE(6)
+        DCCONV_NARROW_CASE(7)
+        DCCONV_NARROW_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef DCCONV_NARROW_CASE
+}
+
 }  // namespace
 
 hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activation, hipStream_t stream,
@@ -450,6 +615,17 @@ hipError_t launch_update(const UpdateParams &p, StateLayout layout, int activati
     const bool rows_v8 = (p.d % kChPerLane == 0) && (p.ld % kChPerLane == 0);
     const bool silu = activation == DCCONV_ACT_SILU;
     const int tiles_v8 = (p.d + kChPerWave - 1) / kChPerWave;
+    // A batch whose 512-channel waves would not cover the CUs spreads over
+    // 128-channel waves instead.
+    const bool narrow = (int64_t)p.n * tiles_v8 <= kNarrowMaxWaves;
+    if (narrow && rows_v8 && p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8 &&
+        (layout == StateLayout::Compact || (int64_t)p.l * p.st_l * 2 < (int64_t)1 << 30)) {
+        const bool cl = layout == StateLayout::ChannelLast;
+        return silu ? (cl ? launch_narrow<DCCONV_ACT_SILU, true>(p, stream, kernel_name)
+                          : launch_narrow<DCCONV_ACT_SILU, false>(p, stream, kernel_name))
+                    : (cl ? launch_narrow<DCCONV_ACT_IDENTITY, true>(p, stream, kernel_name)
+                          : launch_narrow<DCCONV_ACT_IDENTITY, false>(p, stream, kernel_name));
+    }
     if (layout == StateLayout::Compact && rows_v8 && p.st_s % kChPerLane == 0 && p.l >= 3 && p.l <= 8) {
         return silu ? launch_compact<DCCONV_ACT_SILU>(p, tiles_v8, stream, kernel_name)
                     : launch_compact<DCCONV_ACT_IDENTITY>(p, tiles_v8, stream, kernel_name);

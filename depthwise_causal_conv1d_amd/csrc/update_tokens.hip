@@ -9,7 +9,7 @@
 // once instead of T times: per active channel-row the bytes drop from
 // T * (4 + 4L) + 2T to 4L + 4T (compact layout).
 //
-//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP, SPLIT, PREFETCH>: one wavefront owns
+//  * tokens_v8<L, ACT, HAS_BIAS, CHANNEL_LAST, R, KP, SPLIT, PREFETCH, INDEXED>: one wavefront owns
 //    R rows of one 512-channel tile (8 channels per lane), the block shares the
 //    tile's weights.  With SPLIT (one row per block, T >= 2L) the block's two
 //    waves share one row and split its tokens at h = T/2: outputs from token 3
@@ -44,7 +44,7 @@ namespace {
 constexpr uint32_t kBadToken = 1u << 30;
 constexpr uint32_t kBadLane = 1u << 31;
 
-template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP, bool SPLIT, bool PREFETCH>
+template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP, bool SPLIT, bool PREFETCH, bool INDEXED>
 __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_per_row, int64_t block_units) {
     static_assert(!SPLIT || R == 1, "a split block holds one row");
     static_assert(!PREFETCH || R == 1, "only one-row waves prefetch");
@@ -73,13 +73,6 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
         const int lanes_used = min(kWave, (p.d - c0) / kChPerLane);
         const uint32_t vec_bytes = (uint32_t)lanes_used * 16u;
         const uint32_t lane_off = lane < lanes_used ? lane_bytes : kBadLane;
-        int slot[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = group * R + r;
-            slot[r] = __builtin_amdgcn_readfirstlane(row < p.n ? route_row(p.idx, p.status, p.n, p.s, row, lane) : -2);
-        }
-
         // every load of the first pass up front: weights, bias, each row's
         // state (or, for the second half of a split row, the three tokens
         // before it) and its first KP tokens
@@ -90,14 +83,31 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
         if (HAS_BIAS) bv = buffer_load<kCached>(make_buffer(p.bias + c0, vec_bytes), lane_bytes);
         Buffer sbuf[R], xbuf[R], obuf[R];
         u32x4 sv[R][L], xv[R][KP], hx[3];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const bool live = slot[r] >= 0;
+        int slot[R];
+        // x and out of a row: one descriptor each, spanning every token
+        auto x_descriptors = [&](int r) {
+            const bool row_ok = group * R + r < p.n;
             const int row = min(group * R + r, p.n - 1);
-            // x and out of this row: one descriptor each, spanning every token
-            xbuf[r] = make_buffer(p.x + (int64_t)row * p.xs_n + c0, live ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+            xbuf[r] = make_buffer(p.x + (int64_t)row * p.xs_n + c0, row_ok ? x_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
             obuf[r] = make_buffer(p.out + (int64_t)row * p.os_n + c0,
-                                  slot[r] != -2 ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+                                  row_ok ? o_tok * (uint32_t)(p.t - 1) + vec_bytes : 0u);
+        };
+        auto load_x = [&](int r) {
+            if (!CHANNEL_LAST && !reads_state) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) hx[k] = buffer_load<kStream>(xbuf[r], x_tok * (uint32_t)(tb - 3 + k) + lane_off);
+            }
+#pragma unroll
+            for (int i = 0; i < KP; ++i)
+                xv[r][i] = buffer_load<kStream>(xbuf[r], (tb + i < te ? x_tok * (uint32_t)(tb + i) : kBadToken) + lane_off);
+        };
+        auto route = [&](int r) {
+            const int row = group * R + r;
+            slot[r] = __builtin_amdgcn_readfirstlane(
+                row < p.n ? route_row(INDEXED ? p.idx : nullptr, p.status, p.n, p.s, row, lane) : -2);
+        };
+        auto load_state = [&](int r) {
+            const bool live = slot[r] >= 0;
             // State: compact = the tile's contiguous run of L KiB, read coalesced;
             // channel-last = planes kFirst..L-1 of this tile.
             if (CHANNEL_LAST) {
@@ -128,13 +138,21 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
                         sv[r][j] = buffer_load<kStream>(sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
                 }
             }
-            if (!CHANNEL_LAST && !reads_state) {
+        };
+        if constexpr (!INDEXED) {
+            // row r uses slot r: each row's state, then its tokens, in row order
 #pragma unroll
-                for (int k = 0; k < 3; ++k) hx[k] = buffer_load<kStream>(xbuf[r], x_tok * (uint32_t)(tb - 3 + k) + lane_off);
-            }
+            for (int r = 0; r < R; ++r) x_descriptors(r), route(r), load_state(r), load_x(r);
+        } else {
+            // the tokens ahead of the index table, whose latency they then
+            // share; the state once the slots are known (x of a padding row is
+            // read but not used)
 #pragma unroll
-            for (int i = 0; i < KP; ++i)
-                xv[r][i] = buffer_load<kStream>(xbuf[r], (tb + i < te ? x_tok * (uint32_t)(tb + i) : kBadToken) + lane_off);
+            for (int r = 0; r < R; ++r) x_descriptors(r), load_x(r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) route(r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) load_state(r);
         }
         __builtin_amdgcn_s_setprio(0);
 
@@ -323,11 +341,17 @@ template <int L, int ACT, bool CL, int R, int KP, bool SPLIT, bool PREFETCH>
 hipError_t launch_tokens_l(const TokensParams &p, int tiles, hipStream_t stream) {
     const int64_t rows_per_block = SPLIT ? 1 : kWavesPerBlock * R;
     const int64_t block_units = tiles * (((int64_t)p.n + rows_per_block - 1) / rows_per_block);
+    if (p.idx != nullptr)
+        return p.bias != nullptr
+                   ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP, SPLIT, PREFETCH, true>, p, tiles, block_units,
+                                   kBlock, stream)
+                   : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP, SPLIT, PREFETCH, true>, p, tiles, block_units,
+                                   kBlock, stream);
     return p.bias != nullptr
-               ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP, SPLIT, PREFETCH>, p, tiles, block_units, kBlock,
-                               stream)
-               : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP, SPLIT, PREFETCH>, p, tiles, block_units, kBlock,
-                               stream);
+               ? launch_tokens(tokens_v8<L, ACT, true, CL, R, KP, SPLIT, PREFETCH, false>, p, tiles, block_units,
+                               kBlock, stream)
+               : launch_tokens(tokens_v8<L, ACT, false, CL, R, KP, SPLIT, PREFETCH, false>, p, tiles, block_units,
+                               kBlock, stream);
 }
 
 // A grid of one row per wave below this many waves (under two per SIMD) splits

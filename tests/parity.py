@@ -21,6 +21,24 @@ from depthwise_causal_conv1d_amd.workloads import FILL_SENTINEL, bf16_bits_to_f3
 GUARD = 64  # elements of sentinel on each side of every written device buffer (128 B)
 
 
+def _narrow_max_waves() -> int:
+    import os
+    import re
+
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "depthwise_causal_conv1d_amd", "csrc", "device_common.h")
+    return int(re.search(r"kNarrowMaxWaves\s*=\s*(\d+)", open(path).read()).group(1))
+
+
+# The one-token update takes the 128-channel (narrow) form when rows x
+# 512-channel tiles is at most this; above it, the 512-channel kernels.
+NARROW_MAX_WAVES = _narrow_max_waves()
+
+
+def takes_narrow(n: int, d: int) -> bool:
+    return n * ((d + 511) // 512) <= NARROW_MAX_WAVES
+
+
 def to_dev(bits: np.ndarray, dev="cuda") -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
     return t.view(torch.bfloat16)

@@ -22,7 +22,7 @@ import torch
 import oracle
 import depthwise_causal_conv1d_amd as dc
 from depthwise_causal_conv1d_amd import workloads as wl
-from parity import GUARD, assert_outputs_match, from_dev, to_dev
+from parity import GUARD, assert_outputs_match, from_dev, to_dev, takes_narrow
 
 pytestmark = pytest.mark.gpu
 
@@ -117,10 +117,13 @@ def _x_rows(x_rows):
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
 @pytest.mark.parametrize("L,act", [(3, "silu"), (4, None)])
-def test_update_past_4gib(layout, L, act):
-    # D = 1032: two full 512-channel tiles and a ragged 8-channel tile
+@pytest.mark.parametrize("D", [1032, 87560])
+def test_update_past_4gib(layout, L, act, D):
+    # D = 1032: two full 512-channel tiles and a ragged 8-channel tile (three
+    # rows of it take the narrow form); D = 87560: 171 full tiles and a ragged
+    # one, which three rows take in the 512-channel kernels
     rng = np.random.default_rng(700 + L)
-    N, D, S = 3, 1032, 2
+    N, S = 3, 2
     x = _bf(rng, (N, D))
     w = _bf(rng, (D, 4))
     b = _bf(rng, (D,), 0.1)
@@ -136,7 +139,8 @@ def test_update_past_4gib(layout, L, act):
                                 conv_state_indices=torch.from_numpy(INDICES).cuda(), dev_status=status)
     kernel = dc.dcconv_last_kernel()
     torch.cuda.synchronize()
-    assert "_v8" in kernel, kernel
+    assert ("update_narrow" if takes_narrow(N, D) else "_v8") in kernel, kernel
+    assert takes_narrow(N, D) == (D == 1032)
     assert int(status.item()) == 0
     assert_outputs_match(from_dev(out), ref, ref32, exact=act is None)
     _check_state(sbuf, ref_state, layout)

@@ -19,7 +19,7 @@ import oracle
 import depthwise_causal_conv1d_amd as dc
 from depthwise_causal_conv1d_amd import workloads as wl
 from parity import (Case, assert_outputs_match, from_dev, guarded_copy, guarded_empty, to_dev,
-                    assert_guards_intact)
+                    assert_guards_intact, takes_narrow, NARROW_MAX_WAVES)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,7 +70,8 @@ def test_configs_single_step(spec):
                 indices=data["indices"], act=spec.act, status=data["indices"] is not None)
     status = case.check()
     assert status in (None, 0)
-    assert "compact_v8" in case.kernel, case.kernel
+    form = "update_narrow" if takes_narrow(spec.N, spec.D) else "update_compact_v8"
+    assert case.kernel.startswith(form), case.kernel
 
 
 def test_config_long_history_sequential():
@@ -97,13 +98,28 @@ def test_config_long_history_sequential():
 # ------------------------------------------------------------------- edge cases
 
 
+# Rows for each form at D = 1544 (4 tiles of 512 channels): 5 rows take the
+# narrow form, a few more rows than the narrow form's limit allows the
+# 512-channel kernel.
+FORMS = {"narrow": 5, "wide": NARROW_MAX_WAVES // 4 + 12}
+FORM_KERNEL = {"narrow": "update_narrow", "wide": "_v8"}
+
+
+def test_form_rows_straddle_the_threshold():
+    assert takes_narrow(FORMS["narrow"], 1544) and not takes_narrow(FORMS["wide"], 1544)
+    assert 4 * FORMS["wide"] > NARROW_MAX_WAVES
+
+
+@pytest.mark.parametrize("form", ["narrow", "wide"])
 @pytest.mark.parametrize("L", [3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("act", [None, "silu"])
-def test_vector_path_every_l(L, act):
+def test_vector_path_every_l(L, act, form):
     # D = 1544 = 3 full 512-channel tiles + a 8-channel ragged tail tile
-    case = make_case(100 + L, N=5, D=1544, L=L, S=9, bias=True, routing="padded", n_pad=2, act=act)
+    # (12 full 128-channel tiles + the same tail for the narrow form)
+    N = FORMS[form]
+    case = make_case(100 + L, N=N, D=1544, L=L, S=N + 4, bias=True, routing="padded", n_pad=2 + N // 10, act=act)
     case.check()
-    assert "compact_v8" in case.kernel
+    assert FORM_KERNEL[form] in case.kernel and "compact" in case.kernel, case.kernel
 
 
 @pytest.mark.parametrize("D", [1, 7, 13, 100, 1001])
@@ -117,18 +133,23 @@ def test_scalar_path_any_d(D, L):
 
 @pytest.mark.parametrize("L", [3, 4, 6])
 @pytest.mark.parametrize("act", [None, "silu"])
-def test_channel_last_layout(L, act):
-    case = make_case(300 + L, N=7, D=1032, L=L, S=12, layout="channel_last", routing="padded", n_pad=3,
+@pytest.mark.parametrize("form", ["narrow", "wide"])
+def test_channel_last_layout(L, act, form):
+    N = {"narrow": 7, "wide": NARROW_MAX_WAVES // 3 + 9}[form]  # D = 1032: 3 tiles of 512 (2 full + 8 channels)
+    case = make_case(300 + L, N=N, D=1032, L=L, S=N + 5, layout="channel_last", routing="padded", n_pad=3,
                      bias=True, act=act)
     case.check()
-    assert "channel_last_v8" in case.kernel
+    assert FORM_KERNEL[form] in case.kernel and "channel_last" in case.kernel, case.kernel
 
 
+@pytest.mark.parametrize("form", ["narrow", "wide"])
 @pytest.mark.parametrize("L", [5, 7, 8])
-def test_channel_last_more_l(L):
-    case = make_case(320 + L, N=5, D=1544, L=L, S=9, layout="channel_last", routing="unique", bias=False, act="silu")
+def test_channel_last_more_l(L, form):
+    N = FORMS[form]
+    case = make_case(320 + L, N=N, D=1544, L=L, S=N + 4, layout="channel_last", routing="unique", bias=False,
+                     act="silu")
     case.check()
-    assert "channel_last_v8" in case.kernel
+    assert FORM_KERNEL[form] in case.kernel and "channel_last" in case.kernel, case.kernel
 
 
 @pytest.mark.parametrize("layout", ["compact", "channel_last"])
