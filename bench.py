@@ -666,6 +666,9 @@ def main():
     ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--no-copy-control", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0)
+    ap.add_argument("--only-workload", action="store_true",
+                    help="time the workload alone (no copy control, other workloads, CPU baseline, warm-cache "
+                         "run or launch floor): for profiling runs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -693,6 +696,8 @@ def main():
     replays = args.replays if args.replays > 0 else min(200, max(5, math.ceil(2000 / args.steps)))
     other_replays = max(5, replays // 2)
     head = Head()
+    if args.only_workload:
+        args.no_copy_control = args.no_other_workloads = args.no_cpu_baseline = True
     copy = not args.no_copy_control
     spec = wl.BY_NAME[args.workload]
     res, host = measure(spec, args.steps, args.warmup, args.rotate_mb, args.launch, replays, head, copy)
@@ -734,16 +739,19 @@ def main():
 
     # the same calls on one buffer set, resident in the 256 MB Infinity Cache: a
     # cache figure, reported beside the HBM one and never as a fraction of HBM peak
-    warm, _ = measure(spec, args.steps, args.warmup, 0.0, args.launch, other_replays, head)
-    log(f"[bench] {spec.name} warm (one buffer set, Infinity Cache resident): {warm['us_per_call']:.3f} us/call")
-    floor = launch_floor(args.steps, other_replays, args.launch, head)
-    floor_us = floor["median"]
+    warm, floor_us = None, float("nan")
+    if not args.only_workload:
+        warm, _ = measure(spec, args.steps, args.warmup, 0.0, args.launch, other_replays, head)
+        log(f"[bench] {spec.name} warm (one buffer set, Infinity Cache resident): {warm['us_per_call']:.3f} us/call")
+        floor_us = launch_floor(args.steps, other_replays, args.launch, head)["median"]
     # under a profiler every launch carries the tracer's own cost, so the floor can
     # reach the call's period; the split is then meaningless
-    rest_us = res["us_per_call"] - floor_us
-    share = f"{res['bytes_per_call'] / (rest_us * 1e3):.1f} GB/s" if rest_us > 0.1 * res["us_per_call"] else "n/a"
-    log(f"[bench] launch floor (empty fill kernel, graph replay): {floor_us:.3f} us/call; "
-        f"{spec.name} in-kernel share: {share}")
+    have_floor = math.isfinite(floor_us)
+    if have_floor:
+        rest_us = res["us_per_call"] - floor_us
+        share = f"{res['bytes_per_call'] / (rest_us * 1e3):.1f} GB/s" if rest_us > 0.1 * res["us_per_call"] else "n/a"
+        log(f"[bench] launch floor (empty fill kernel, same launch method): {floor_us:.3f} us/call; "
+            f"{spec.name} in-kernel share: {share}")
     traffic = read_traffic(res["kernel"], spec.name)
     line = {
         "metric": METRIC,
@@ -776,11 +784,13 @@ def main():
             "frac_of_copy": round(res["frac_of_copy"], 4)},
         # per-call floor of a graph-replayed launch, measured beside the workload: a call of
         # B bytes cannot exceed B / (B / peak + floor), the ceiling the fraction is read against
-        "launch_floor_us": round(floor_us, 3),
-        "warm_cache": {"us_per_call": round(warm["us_per_call"], 4), "gbs": round(warm["gbs"], 1),
-                       "buffer_sets": warm["buffer_sets"], "note": "Infinity Cache resident, not an HBM figure"},
+        "launch_floor_us": round(floor_us, 3) if have_floor else None,
+        "warm_cache": None if warm is None else {
+            "us_per_call": round(warm["us_per_call"], 4), "gbs": round(warm["gbs"], 1),
+            "buffer_sets": warm["buffer_sets"], "note": "Infinity Cache resident, not an HBM figure"},
         "frac_ceiling_at_floor": round(res["bytes_per_call"] / (res["bytes_per_call"] / (PEAK_HBM_GBS * 1e3)
-                                                                + floor_us) / (PEAK_HBM_GBS * 1e3), 4),
+                                                                + floor_us) / (PEAK_HBM_GBS * 1e3), 4)
+        if have_floor else None,
         "cpu_baseline": cpu,
         "other_workloads": others,
         "env": environment(),
