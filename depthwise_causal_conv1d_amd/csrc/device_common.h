@@ -226,6 +226,32 @@ __device__ __forceinline__ void weight_tile_share(u32x4 *tile, const u32x4 (&raw
     }
 }
 
+// ---- the compact-state stage ----------------------------------------------------
+// A wave moves a tile's compact state (L 16-byte chunks per lane) through LDS
+// between coalesced order (chunk j*64 + lane, as it is loaded and stored) and
+// per-lane order (chunk lane*L + k: the lane's 8 channels).  A per-lane access
+// steps L chunks from lane to lane; for even L that puts several lanes of one
+// 16-byte access on the same LDS banks (eight at L = 8), so the stage keeps an
+// odd pitch of L | 1 chunks per lane: chunk c of the coalesced order sits at
+// c + c / L when L is even.
+template <int L>
+constexpr int stage_pitch() {
+    return L | 1;
+}
+template <int L>
+constexpr int stage_chunks() {
+    return kWave * stage_pitch<L>();
+}
+template <int L>
+__device__ __forceinline__ int stage_coalesced(int j, int lane) {
+    const int c = j * kWave + lane;
+    return (L & 1) ? c : c + c / L;
+}
+template <int L>
+__device__ __forceinline__ int stage_lane(int lane, int k) {
+    return lane * stage_pitch<L>() + k;
+}
+
 // ---- history planes -----------------------------------------------------------
 // A lane's 8 channels of one history position form a "plane" vector (word q
 // holds channels 2q, 2q+1).  The compact state holds the same values

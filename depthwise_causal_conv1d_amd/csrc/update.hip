@@ -101,7 +101,7 @@ __device__ __forceinline__ void update8(const uint32_t (&hist)[4 * L], const uin
 template <int L, int ACT, int R, bool HAS_BIAS, bool INDEXED>
 __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int tiles_per_row,
                                                             int64_t block_units) {
-    __shared__ u32x4 stage_all[kWavesPerBlock][R][kWave * L];
+    __shared__ u32x4 stage_all[kWavesPerBlock][R][stage_chunks<L>()];
     __shared__ u32x4 weight_tile[4 * kWave];  // the tile's 4 KiB of weights, swizzled
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
         // would also wait for that store to be acknowledged by memory.  Keeping
         // all stores last means no wait ever follows one.
 #pragma unroll
-        for (int j = 0; j < L; ++j) stage_all[wave][0][j * kWave + lane] = sv[0][j];
+        for (int j = 0; j < L; ++j) stage_all[wave][0][stage_coalesced<L>(j, lane)] = sv[0][j];
         u32x4 nv[R][L], ov[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             uint32_t hist[4 * L];
 #pragma unroll
             for (int k = 0; k < L; ++k) {
-                const u32x4 t = stage[lane * L + k];
+                const u32x4 t = stage[stage_lane<L>(lane, k)];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) hist[4 * k + q] = t[q];
             }
@@ -210,13 +210,13 @@ __global__ __launch_bounds__(kBlock) void update_compact_v8(UpdateParams p, int 
             wave_lds_sync();
 #pragma unroll
             for (int k = 0; k < L; ++k)
-                stage[lane * L + k] = u32x4{nhist[4 * k], nhist[4 * k + 1], nhist[4 * k + 2], nhist[4 * k + 3]};
+                stage[stage_lane<L>(lane, k)] = u32x4{nhist[4 * k], nhist[4 * k + 1], nhist[4 * k + 2], nhist[4 * k + 3]};
             wave_lds_sync();
 #pragma unroll
-            for (int j = 0; j < L; ++j) nv[r][j] = stage[j * kWave + lane];
+            for (int j = 0; j < L; ++j) nv[r][j] = stage[stage_coalesced<L>(j, lane)];
             if (r + 1 < R) {
 #pragma unroll
-                for (int j = 0; j < L; ++j) stage_all[wave][r + 1][j * kWave + lane] = sv[r + 1][j];
+                for (int j = 0; j < L; ++j) stage_all[wave][r + 1][stage_coalesced<L>(j, lane)] = sv[r + 1][j];
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // all stores below, after all of the above

@@ -48,7 +48,7 @@ template <int L, int ACT, bool HAS_BIAS, bool CHANNEL_LAST, int R, int KP, bool 
 __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_per_row, int64_t block_units) {
     static_assert(!SPLIT || R == 1, "a split block holds one row");
     static_assert(!PREFETCH || R == 1, "only one-row waves prefetch");
-    __shared__ u32x4 stage_all[kWavesPerBlock][CHANNEL_LAST ? 1 : kWave * L];
+    __shared__ u32x4 stage_all[kWavesPerBlock][CHANNEL_LAST ? 1 : stage_chunks<L>()];
     __shared__ u32x4 weight_tile[4 * kWave];
     // Positions read in the channel-last layout: the first token's taps need
     // L-3..L-1 and the shift needs 1..L-1; position 0 only when it is a tap.
@@ -177,12 +177,12 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
                 u32x4 *stage = stage_all[wave];
                 wave_lds_sync();
 #pragma unroll
-                for (int j = 0; j < L; ++j) stage[j * kWave + lane] = sv[r][j];
+                for (int j = 0; j < L; ++j) stage[stage_coalesced<L>(j, lane)] = sv[r][j];
                 wave_lds_sync();
                 uint32_t h[4 * L];
 #pragma unroll
                 for (int k = 0; k < L; ++k) {
-                    const u32x4 t = stage[lane * L + k];
+                    const u32x4 t = stage[stage_lane<L>(lane, k)];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) h[4 * k + q] = t[q];
                 }
@@ -274,11 +274,12 @@ __global__ __launch_bounds__(kBlock) void tokens_v8(TokensParams p, int tiles_pe
                 from_planes<L>(pl[r], h);
                 wave_lds_sync();
 #pragma unroll
-                for (int k = 0; k < L; ++k) stage[lane * L + k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+                for (int k = 0; k < L; ++k)
+                    stage[stage_lane<L>(lane, k)] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
                 wave_lds_sync();
                 u32x4 nv[L];
 #pragma unroll
-                for (int j = 0; j < L; ++j) nv[j] = stage[j * kWave + lane];
+                for (int j = 0; j < L; ++j) nv[j] = stage[stage_coalesced<L>(j, lane)];
 #pragma unroll
                 for (int j = 0; j < L; ++j)
                     buffer_store<kStream>(nv[j], sbuf[r], (uint32_t)(j * kWave) * 16u + lane_bytes);
