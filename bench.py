@@ -739,6 +739,14 @@ def main():
 
     # the same calls on one buffer set, resident in the 256 MB Infinity Cache: a
     # cache figure, reported beside the HBM one and never as a fraction of HBM peak
+    # the same workload in 1000-step graph replays: the per-call period of long
+    # back-to-back runs, independent of --steps (reported beside the headline,
+    # which stays the K-step figure)
+    steady = None
+    if not args.only_workload and args.steps < 1000:
+        steady, _ = measure(spec, 1000, args.warmup, args.rotate_mb, "graph", 5, head)
+        log(f"[bench] {spec.name} steady state (1000-step graph replays): {steady['us_per_call']:.3f} us/call, "
+            f"{100 * steady['frac']:.1f}% of 8 TB/s")
     warm, floor_us = None, float("nan")
     if not args.only_workload:
         warm, _ = measure(spec, args.steps, args.warmup, 0.0, args.launch, other_replays, head)
@@ -778,6 +786,11 @@ def main():
                    "events": "hipEventDisableSystemFence",
                    "us_per_call": {"p10": round(res["us_p10"], 4), "median": round(res["us_per_call"], 4),
                                    "p90": round(res["us_p90"], 4)}},
+        # 1000-step graph replays of the same workload in the same run (context, not the headline)
+        "steady_state": None if steady is None else {
+            "steps_per_region": 1000, "regions": steady["replays"], "mode": steady["timing_mode"],
+            "us_per_call": round(steady["us_per_call"], 4), "gbs": round(steady["gbs"], 1),
+            "frac": round(steady["frac"], 4)},
         # the same byte count moved by a plain copy, interleaved with the update replay by replay
         "copy_control": None if "copy" not in res else {
             **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["copy"].items()},
