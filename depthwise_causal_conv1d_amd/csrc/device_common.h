@@ -230,13 +230,14 @@ __device__ __forceinline__ void weight_tile_share(u32x4 *tile, const u32x4 (&raw
 // A wave moves a tile's compact state (L 16-byte chunks per lane) through LDS
 // between coalesced order (chunk j*64 + lane, as it is loaded and stored) and
 // per-lane order (chunk lane*L + k: the lane's 8 channels).  A per-lane access
-// steps L chunks from lane to lane; for even L that puts several lanes of one
-// 16-byte access on the same LDS banks (eight at L = 8), so the stage keeps an
-// odd pitch of L | 1 chunks per lane: chunk c of the coalesced order sits at
-// c + c / L when L is even.
+// steps L chunks from lane to lane; at L = 8 (128 bytes) that puts every lane
+// of a 16-byte access on the same LDS banks, so the stage keeps a pitch of 9
+// chunks per lane there: chunk c of the coalesced order sits at c + c / 8.
+// (Smaller even L conflict less and gain nothing from a pitch of L + 1, which
+// costs LDS: at L = 4 a two-row block would grow from 20 to 24 KiB.)
 template <int L>
 constexpr int stage_pitch() {
-    return L | 1;
+    return L == 8 ? L + 1 : L;
 }
 template <int L>
 constexpr int stage_chunks() {
@@ -245,7 +246,7 @@ constexpr int stage_chunks() {
 template <int L>
 __device__ __forceinline__ int stage_coalesced(int j, int lane) {
     const int c = j * kWave + lane;
-    return (L & 1) ? c : c + c / L;
+    return stage_pitch<L>() == L ? c : c + c / L;
 }
 template <int L>
 __device__ __forceinline__ int stage_lane(int lane, int k) {
