@@ -11,25 +11,31 @@
 // coalesced 16-byte accesses and around keeping many of them in flight, not
 // around arithmetic (there is no contraction, so no MFMA).
 //
-//  * update_compact_v8<L, ACT, R>: the fast path for the compact [S, D, L] layout.
-//    One wavefront owns R rows of one 512-channel tile; each lane owns 8 adjacent
-//    channels, so x, weight, bias and out move as one 16-byte vector per lane.
-//    A row's tile of state is a contiguous 1 KiB * L run.  The wave issues every
-//    load of its R rows up front (weights and bias once for all R rows), then
-//    finishes the rows in order, each as soon as its own loads have landed: the
-//    state run goes through a per-wave LDS stage (written in coalesced order,
-//    read back in per-lane channel order), is shifted in registers with byte
-//    permutes, goes back through the stage and leaves with L coalesced 16-byte
-//    stores.  Waves never share LDS, so all synchronisation is wave-local.
-//    The single-use streams (x, state, out) carry the non-temporal hint, which
-//    keeps them from displacing the reused weights and routing table in the
-//    caches.
-//  * update_channel_last_v8<L, ACT, R>: the [S, L, D] layout a prefill hands
-//    over.  Every history position is a contiguous plane over channels, so the
-//    lane that owns 8 channels loads and stores each plane with one coalesced
-//    16-byte access and the shift is a renaming of planes; no state goes through
-//    LDS, and position 0 is not read unless it is a tap (L = 3).  The same block
-//    structure, weight sharing and store ordering as the compact kernel.
+//  * update_compact_v8<L, ACT, R, HAS_BIAS, INDEXED>: the fast path for the
+//    compact [S, D, L] layout.  One wavefront owns R rows of one 512-channel
+//    tile; each lane owns 8 adjacent channels, so x, weight, bias and out move as
+//    one 16-byte vector per lane.  A row's tile of state is a contiguous
+//    1 KiB * L run.  The wave issues every load of its R rows up front (weights
+//    and bias once for all R rows; with an index table, every x before the table
+//    is read and the state runs after), then finishes the rows in order, each as
+//    soon as its own loads have landed: the state run goes through a per-wave
+//    LDS stage (written in coalesced order, read back in per-lane channel order),
+//    is shifted in registers with byte permutes, goes back through the stage and
+//    leaves with L coalesced 16-byte stores.  Waves never share LDS, so all
+//    synchronisation is wave-local.  The single-use streams (x, state, out)
+//    carry the non-temporal hint, which keeps them from displacing the reused
+//    weights and routing table in the caches.
+//  * update_channel_last_v8<L, ACT, R, HAS_BIAS, INDEXED>: the [S, L, D] layout
+//    a prefill hands over.  Every history position is a contiguous plane over
+//    channels, so the lane that owns 8 channels loads and stores each plane with
+//    one coalesced 16-byte access and the shift is a renaming of planes; no state
+//    goes through LDS, and position 0 is not read unless it is a tap (L = 3).
+//    The same block structure, weight sharing and store ordering as the compact
+//    kernel.
+//  * update_narrow<L, ACT, HAS_BIAS, CHANNEL_LAST>: small batches (at most
+//    kNarrowMaxWaves 512-channel waves).  One wavefront per (row, 128-channel
+//    tile), 2 channels per lane: four times the waves, each with a short chain
+//    and no LDS or block barrier (see below).
 //  * update_scalar<ACT>: one thread per (row, channel), any stride, any L >= 3,
 //    any D.  Serves what the vector paths do not (D or row stride not a multiple
 //    of 8, L > 8).
