@@ -669,6 +669,8 @@ def main():
     ap.add_argument("--only-workload", action="store_true",
                     help="time the workload alone (no copy control, other workloads, CPU baseline, warm-cache "
                          "run or launch floor): for profiling runs")
+    ap.add_argument("--keep-copy-control", action="store_true",
+                    help="with --only-workload, still interleave the copy control (a trace then holds both)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -697,7 +699,8 @@ def main():
     other_replays = max(5, replays // 2)
     head = Head()
     if args.only_workload:
-        args.no_copy_control = args.no_other_workloads = args.no_cpu_baseline = True
+        args.no_other_workloads = args.no_cpu_baseline = True
+        args.no_copy_control = args.no_copy_control or not args.keep_copy_control
     copy = not args.no_copy_control
     spec = wl.BY_NAME[args.workload]
     res, host = measure(spec, args.steps, args.warmup, args.rotate_mb, args.launch, replays, head, copy)
