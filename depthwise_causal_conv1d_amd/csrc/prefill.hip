@@ -28,7 +28,7 @@
 //    short dependent chains run under the chunk blocks' streaming.
 // prefill_sweep_v8<L, ACT, layout, HAS_BIAS> (the sweep form, for rows of at
 // most 4096 channels or columns of at most 64 tokens): blocks of four waves,
-// as many as the GPU holds at once, walk (32-token group, tile) items in
+// as many as the GPU holds at once, walk (16-token group, tile) items in
 // memory order, so every block does nearly the same work and the grid reads
 // one compact stretch of x at a time; a group's halo comes from the previous
 // wave through LDS (see sweep_block).  Its edge blocks come after the sweep
@@ -264,11 +264,15 @@ __device__ __forceinline__ void chunk_block(const PrefillParams &p, u32x4 *weigh
 
 // ---- the sweep role ---------------------------------------------------------
 // Tokens per wave and waves per block of the sweep role; an item is kSweepSpan
-// consecutive tokens of one 512-channel tile.
-constexpr int kSweepG = 8;
+// consecutive tokens of one 512-channel tile.  Four tokens per wave keep the
+// kernel at 123 VGPRs, four waves per SIMD (eight tokens: 143, three).  A wave
+// hands its last three tokens to the next as that wave's halo, so it must own
+// at least three.
+constexpr int kSweepG = 4;
 constexpr int kSweepWaves = 4;
 constexpr int kSweepSpan = kSweepG * kSweepWaves;
 constexpr int kSweepBlock = kWave * kSweepWaves;
+static_assert(kSweepG >= 3, "a wave's last three tokens are the next wave's halo");
 
 // This lane's 8 channels x 4 taps (64 contiguous bytes of the [D, 4] weight) as
 // FP32, channel-major; zeros for a lane past a ragged tile.
@@ -686,22 +690,17 @@ int resident_blocks(const void *kernel, int block, int (&cache)[kMaxDevices]) {
     return n;
 }
 
-// The sweep grid: a multiple of `tiles` within [cap / 2, cap] (cap = the blocks
-// resident at once) that pads `items` least, the larger on a tie; every block
-// then does ceil(items / grid) or one fewer items.
+// The sweep grid: every block the GPU holds at once (cap), rounded down to a
+// multiple of `tiles` so a block keeps one tile, or one block per item when
+// there are fewer.  Every block then does ceil(items / grid) or one fewer
+// items.  (Trading residency for whole rounds -- the multiple of `tiles` in
+// [cap / 2, cap] that pads the item count least -- measured slower: with two
+// blocks per CU instead of four, 8 x 2048 tokens at D = 4096 took 58.8 us
+// against 51.3.)
 int64_t sweep_grid(int64_t items, int tiles, int64_t cap) {
     const int64_t gmax = cap / tiles * tiles;
     if (gmax < tiles) return 0;
-    if (items <= gmax) return items;
-    int64_t best = gmax, best_cost = (items + gmax - 1) / gmax * gmax;
-    for (int64_t g = gmax - tiles; g >= gmax / 2 && g >= tiles; g -= tiles) {
-        const int64_t cost = (items + g - 1) / g * g;
-        if (cost < best_cost) {
-            best = g;
-            best_cost = cost;
-        }
-    }
-    return best;
+    return items <= gmax ? items : gmax;
 }
 
 // Column (chunk) or sweep form.  A/B on MI355X: the sweep wins where rows are

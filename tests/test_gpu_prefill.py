@@ -132,7 +132,7 @@ class PrefillCase:
 
 
 @pytest.mark.parametrize("L", [3, 4, 8])
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 31, 32, 33, 70])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 15, 16, 17, 31, 32, 33, 70])
 def test_prefill_batch_compact(L, T):
     case = PrefillCase(2000 + 10 * L + T, 1096, N=3, T=T, L=L, state="compact", bias=T % 2 == 0,
                        act=None if T % 3 == 0 else "silu")
@@ -187,8 +187,9 @@ def test_prefill_sweep_form_wide_short(layout):
 
 
 def test_prefill_sweep_packed_many_short_sequences():
-    """Packed sequences shorter than a sweep item (32 tokens): items span many
-    sequences, and a wave's 8 tokens cross several boundaries."""
+    """Packed sequences shorter than a sweep item (16 tokens): items span many
+    sequences, and a wave's 4 tokens cross several boundaries (empty and
+    one-token sequences among them)."""
     rng = np.random.default_rng(2280)
     lens = [int(v) for v in rng.integers(0, 12, size=700)]
     case = PrefillCase(2280, 1032, lens=lens, L=3, state="channel_last", routing="padded", n_pad=40, S=700,
