@@ -209,33 +209,21 @@ class PrefillWorkload:
 
 
 class Head:
-    """A spin kernel enqueued ahead of a timed region: while the GPU spins, the
-    host finishes enqueueing the region's launches, so the start event is
-    followed directly by the first step and the steps run back to back.
-    Calibrated once; ``__call__(us)`` spins for about ``us`` microseconds."""
+    """A busy kernel enqueued ahead of a timed region: while every SIMD runs
+    arithmetic (the library's ``dcconv_busy_spin``, timed by the device's wall
+    clock), the host finishes enqueueing the region's launches, so the start
+    event is followed directly by the first step, the steps run back to back,
+    and the region starts on a chip at its working clocks.  (Behind a one-thread
+    spin the chip idles and the packed prefill region measured about 3 % slower;
+    the decode regions measured the same behind either.)  ``__call__(us)``
+    spins for about ``us`` microseconds."""
 
-    def __init__(self):
-        import torch
-
-        self.cycles_per_us = 0.0
-        if not hasattr(torch.cuda, "_sleep"):
-            return
-        probe = 200_000
-        stream = torch.cuda.current_stream()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(probe)
-        torch.cuda.synchronize()
-        a.record(stream)
-        torch.cuda._sleep(probe)
-        b.record(stream)
-        torch.cuda.synchronize()
-        self.cycles_per_us = probe / max(a.elapsed_time(b) * 1e3, 1e-3)
+    available = True
 
     def __call__(self, us: float):
-        import torch
+        import depthwise_causal_conv1d_amd as dc
 
-        if self.cycles_per_us > 0:
-            torch.cuda._sleep(int(self.cycles_per_us * us))
+        dc.busy_spin(us)
 
 
 class TimingEvent:
@@ -293,7 +281,7 @@ class Timer:
     def __init__(self, step, first: int, steps: int, n_sets: int, launch: str, head: Head):
         self.step, self.first, self.steps, self.head = step, first, steps, head
         self.mode = launch
-        if launch == "graph" and steps <= EAGER_MAX_STEPS and head.cycles_per_us > 0:
+        if launch == "graph" and steps <= EAGER_MAX_STEPS and head.available:
             self.mode = "eager+head"
         self.graphs = capture(step, first, steps, n_sets) if self.mode == "graph" else []
         self.n_regions = max(1, min(16, math.ceil(n_sets / steps)))
@@ -421,7 +409,7 @@ def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str, replay
                tokens_per_call=wk.tokens,
                buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
     res["timing_mode"] = "eager+head" if (launch == "graph" and steps <= EAGER_MAX_STEPS
-                                          and head.cycles_per_us > 0) else launch
+                                          and head.available) else launch
     res["frac"] = res["gbs"] / PEAK_HBM_GBS
     if getattr(wk, "active", spec.N) != spec.N:
         res["active_rows_per_s"] = wk.active * wk.tokens / (ms * 1e-3)

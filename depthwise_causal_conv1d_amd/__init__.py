@@ -30,6 +30,7 @@ __all__ = [
     "dcconv_update_tokens", "causal_conv1d_update", "causal_conv1d_update_out",
     "causal_conv1d_update_tokens", "dcconv_prefill", "causal_conv1d", "library_path", "DcconvError",
     "DCCONV_DEV_BAD_SEQ", "DCCONV_DEV_BAD_SEQLEN", "dcconv_stream_copy", "stream_copy",
+    "dcconv_busy_spin", "busy_spin",
 ]
 
 DCCONV_OK, DCCONV_EINVAL, DCCONV_EUNSUPPORTED, DCCONV_EHIP = 0, 1, 2, 3
@@ -96,6 +97,8 @@ def _load() -> ctypes.CDLL:
                                            vp, vp]                           # dev_status, stream
             lib.dcconv_stream_copy.restype = i32
             lib.dcconv_stream_copy.argtypes = [vp, vp, i64, vp]      # dst, src, bytes, stream
+            lib.dcconv_busy_spin.restype = i32
+            lib.dcconv_busy_spin.argtypes = [ctypes.c_double, vp]     # microseconds, stream
             _lib = lib
     return _lib
 
@@ -151,6 +154,11 @@ def dcconv_prefill(x, n, d, t, xs_n, xs_d, xs_t, seq_starts, conv_state, s, l, s
     return _load().dcconv_prefill(x, n, d, t, xs_n, xs_d, xs_t, seq_starts, conv_state, s, l, st_s, st_d, st_l,
                                   conv_state_indices, has_initial_state, weight, w, bias, activation, out, os_n,
                                   os_d, os_t, dev_status, stream)
+
+
+def dcconv_busy_spin(microseconds, stream) -> int:
+    """The busy-spin measurement control, one to one."""
+    return _load().dcconv_busy_spin(microseconds, stream)
 
 
 def dcconv_stream_copy(dst, src, nbytes, stream) -> int:
@@ -392,4 +400,15 @@ def stream_copy(dst, src) -> None:
     with torch.cuda.device(src.device):
         rc = dcconv_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes,
                                 torch.cuda.current_stream(src.device).cuda_stream)
+    _raise_for(rc)
+
+
+def busy_spin(microseconds: float, device=None) -> None:
+    """Keep every SIMD of the device busy for about ``microseconds`` on its
+    current stream: a benchmark's head ahead of a timed region."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        rc = dcconv_busy_spin(float(microseconds), torch.cuda.current_stream(dev).cuda_stream)
     _raise_for(rc)

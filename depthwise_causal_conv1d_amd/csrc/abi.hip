@@ -406,3 +406,20 @@ extern "C" int dcconv_stream_copy(void *dst, const void *src, int64_t bytes, voi
     if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
     return succeed("stream_copy_v8");
 }
+
+extern "C" int dcconv_busy_spin(double microseconds, void *stream) {
+    if (!(microseconds >= 0.0 && microseconds <= 1e6))
+        return fail(DCCONV_EINVAL, "microseconds=%g is not in [0, 1e6]", microseconds);
+    if (microseconds == 0.0) return succeed("");
+    int dev = 0, khz = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return fail(DCCONV_EHIP, "device query failed: %s", hipGetErrorString(err));
+    if (khz <= 0 || cus <= 0) return fail(DCCONV_EHIP, "device reports wall clock %d kHz, %d CUs", khz, cus);
+    // one wave per SIMD (four per CU)
+    const uint64_t ticks = (uint64_t)(microseconds * (double)khz / 1000.0) + 1;
+    err = dcconv::launch_busy_spin(ticks, 4 * cus, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(DCCONV_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return succeed("busy_spin");
+}

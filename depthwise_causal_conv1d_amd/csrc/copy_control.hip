@@ -12,6 +12,10 @@
 // waves, as the large decode update is; of the shapes tried for a 16.8 MB copy
 // (1, 2 or 4 waves per block, 1 to 16 vectors per lane) this one was the
 // fastest.
+//
+// A second control, busy_spin, keeps every SIMD busy with arithmetic for a
+// given time: enqueued ahead of a timed region it lets the host enqueue the
+// region's launches while the chip stays at its working clocks.
 #include <stdint.h>
 
 #include "dcconv.h"
@@ -44,7 +48,27 @@ __global__ __launch_bounds__(kWave) void stream_copy_v8(uint8_t *dst, const uint
     } while (b < blocks);
 }
 
+// Measurement control: every wave runs FP32 FMAs until `ticks` of the
+// constant-rate wall clock have passed since it started, so the whole chip is
+// busy for the span (a benchmark's head ahead of a timed region).  The chain's
+// result feeds an empty asm statement, which keeps the loop without a store.
+__global__ __launch_bounds__(kWave) void busy_spin(uint64_t ticks) {
+    const uint64_t t0 = wall_clock64();
+    float a = (float)threadIdx.x * 1e-3f;
+    do {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) a = __builtin_fmaf(a, 1.0000001f, 1e-7f);
+    } while (wall_clock64() - t0 < ticks);
+    asm volatile("" : : "v"(a));
+}
+
 }  // namespace
+
+hipError_t launch_busy_spin(uint64_t ticks, int waves, hipStream_t stream) {
+    void *args[] = {&ticks};
+    return hipLaunchKernel(reinterpret_cast<const void *>(busy_spin), dim3((unsigned)waves), dim3(kWave), args, 0,
+                           stream);
+}
 
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream) {
     int64_t blocks = (bytes + kCopyBlockBytes - 1) / kCopyBlockBytes;

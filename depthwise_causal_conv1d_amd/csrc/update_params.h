@@ -80,5 +80,6 @@ hipError_t launch_prefill(const PrefillParams &p, StateLayout layout, int activa
 
 // The measurement control behind dcconv_stream_copy (validated on the host).
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
+hipError_t launch_busy_spin(uint64_t ticks, int waves, hipStream_t stream);
 
 }  // namespace dcconv

@@ -267,6 +267,23 @@ int dcconv_prefill(const void *x, int64_t n, int64_t d, int64_t t,
  */
 int dcconv_stream_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
+/*
+ * dcconv_busy_spin -- measurement control, not part of the operation.
+ * Enqueues a kernel that keeps every SIMD of the current device busy with FP32
+ * arithmetic for about `microseconds` (timed by the device's constant-rate wall
+ * clock).  A benchmark puts it ahead of a timed region: the host enqueues the
+ * region's launches meanwhile, and the region starts on a chip at its working
+ * clocks.  (Behind a one-thread spin the chip idles, and the prefill, whose
+ * arithmetic is a large part of its time, measured 3 % slower in the region.)
+ *
+ * microseconds  0 <= microseconds <= 1e6; 0 returns DCCONV_OK and enqueues
+ *               nothing.
+ * stream        hipStream_t (NULL = the null stream); asynchronous.
+ *
+ * Returns DCCONV_OK, DCCONV_EINVAL (out of range or NaN) or DCCONV_EHIP.
+ */
+int dcconv_busy_spin(double microseconds, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

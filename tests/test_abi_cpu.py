@@ -340,3 +340,12 @@ def test_stream_copy_refusals_before_any_hip_call():
     assert dc.dcconv_stream_copy(0, b, 16, None) == dc.DCCONV_EINVAL
     assert dc.dcconv_stream_copy(a, b, 0, None) == dc.DCCONV_OK
     assert dc.dcconv_last_kernel() == ""
+
+
+def test_busy_spin_refusals_before_any_hip_call():
+    # out-of-range spans are refused on the host; 0 enqueues nothing
+    for us in (-1.0, float("nan"), float("inf"), 1e6 + 1):
+        assert dc.dcconv_busy_spin(us, None) == dc.DCCONV_EINVAL
+        assert "microseconds" in dc.dcconv_last_error()
+    assert dc.dcconv_busy_spin(0.0, None) == dc.DCCONV_OK
+    assert dc.dcconv_last_kernel() == ""

@@ -24,3 +24,19 @@ def test_stream_copy_copies_exactly(nbytes):
     assert dc.dcconv_last_kernel() == "stream_copy_v8"
     assert torch.equal(dst, src)
     assert bool((buf[:GUARD] == 0xA5).all()) and bool((buf[GUARD + nbytes:] == 0xA5).all())
+
+
+@pytest.mark.parametrize("us", [50.0, 400.0])
+def test_busy_spin_lasts_about_as_asked(us):
+    """The benchmark's head: it must hold the stream for about the time asked
+    (wall-clock bound, whatever the shader clock) and then end."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dc.busy_spin(1.0)  # first launch out of the timing
+    a.record(stream)
+    dc.busy_spin(us)
+    b.record(stream)
+    torch.cuda.synchronize()
+    assert dc.dcconv_last_kernel() == "busy_spin"
+    took = a.elapsed_time(b) * 1e3
+    assert 0.9 * us <= took <= us + 200.0, took
