@@ -34,6 +34,6 @@ def test_bench_prints_one_complete_json_line():
     t = d["timing"]
     assert t["steps_per_region"] == 20 and t["regions"] >= 5
     assert t["us_per_call"]["p10"] <= t["us_per_call"]["median"] <= t["us_per_call"]["p90"]
-    assert abs(d["ms_per_step"] * 1e3 - t["us_per_call"]["median"]) < 1e-6
+    assert abs(d["ms_per_step"] * 1e3 - t["us_per_call"]["median"]) < 1e-4  # the median is rounded to 4 places
     assert d["copy_control"]["us_per_call"] > 0 and d["copy_control"]["frac_of_copy"] > 0
     assert d["steady_state"]["steps_per_region"] == 1000
