@@ -14,11 +14,11 @@ Infinity Cache, so consecutive steps cycle through enough independent buffer set
 Timing: a timed region is exactly K steps, bracketed by device
 synchronisations and timed with HIP events (created without the system-scope
 fence, which the timed work does not need) on the stream that launches the
-kernels.  Up to 256 steps the region's launches go straight to the stream
+kernels.  Up to 32 steps the region's launches go straight to the stream
 behind a busy kernel (every SIMD running arithmetic) that holds the GPU until
 the host has enqueued them all, so the steps run back to back on a chip at its
-working clocks; a HIP graph replay would add a fixed 10-25 us per region here,
-half a microsecond per step at K = 20.  Longer regions are
+working clocks; a HIP graph replay would add about 7 us per region here,
+a third of a microsecond per step at K = 20.  Longer regions are
 replayed from HIP graphs (several, when the buffer sets outnumber K, so the
 regions keep cycling through every set).  The per-step time reported is the
 median over the regions, with p10 and p90.  A plain copy of the same byte count
@@ -271,9 +271,11 @@ class TimingEvent:
 
 # Up to this many steps a timed region is launched directly on the stream behind
 # the busy head (every launch then fits in the hardware queue while the GPU
-# spins); longer regions are replayed from a HIP graph, whose fixed cost per
-# replay (about 10-25 us here) is then below 0.1 us per step.
-EAGER_MAX_STEPS = 256
+# spins); longer regions are replayed from a HIP graph.  A replay costs about
+# 7 us once behind the busy head, and a graph node 0.14-0.48 us less than a
+# direct launch, so graphs win from about 35 steps on (large decode: 20 steps
+# 6.41 direct against 6.58 as a graph, 100 steps 6.43 against 6.29).
+EAGER_MAX_STEPS = 32
 
 
 class Timer:
