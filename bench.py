@@ -278,15 +278,22 @@ class TimingEvent:
 EAGER_MAX_STEPS = 32
 
 
+def timing_mode(launch: str, steps: int, head_available: bool) -> str:
+    """How a region of ``steps`` steps is launched: ``eager`` when asked for,
+    else direct launches behind the head (``eager+head``) up to EAGER_MAX_STEPS
+    steps, else ``graph``."""
+    if launch == "graph" and steps <= EAGER_MAX_STEPS and head_available:
+        return "eager+head"
+    return launch
+
+
 class Timer:
     """Times regions of exactly K steps: K launches between two timing events,
     bracketed by device synchronisations, returning microseconds per step."""
 
     def __init__(self, step, first: int, steps: int, n_sets: int, launch: str, head: Head):
         self.step, self.first, self.steps, self.head = step, first, steps, head
-        self.mode = launch
-        if launch == "graph" and steps <= EAGER_MAX_STEPS and head.available:
-            self.mode = "eager+head"
+        self.mode = timing_mode(launch, steps, head.available)
         self.graphs = capture(step, first, steps, n_sets) if self.mode == "graph" else []
         self.n_regions = max(1, min(16, math.ceil(n_sets / steps)))
         # host time to enqueue one step, for sizing the spin ahead of an eager region
@@ -416,8 +423,7 @@ def measure(spec, steps: int, warmup: int, rotate_mb: float, launch: str, replay
                rows_per_s=getattr(wk, "rows", spec.N * wk.tokens) / (ms * 1e-3),
                tokens_per_call=wk.tokens,
                buffer_sets=wk.n_sets, set_bytes=wk.set_bytes)
-    res["timing_mode"] = "eager+head" if (launch == "graph" and steps <= EAGER_MAX_STEPS
-                                          and head.available) else launch
+    res["timing_mode"] = timing_mode(launch, steps, head.available)
     res["frac"] = res["gbs"] / PEAK_HBM_GBS
     if getattr(wk, "active", spec.N) != spec.N:
         res["active_rows_per_s"] = wk.active * wk.tokens / (ms * 1e-3)

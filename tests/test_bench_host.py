@@ -165,3 +165,15 @@ def test_kernel_hash_ignores_comments_but_not_code():
     assert bench._code_only(code) == bench._code_only(code.replace("adds one", "increments"))
     assert bench._code_only(code) == bench._code_only("int f(int a) {\n\n    return a + 1;\n}\n")
     assert bench._code_only(code) != bench._code_only(code.replace("a + 1", "a + 2"))
+
+
+def test_timing_mode_direct_up_to_32_steps_then_graphs():
+    # short regions go straight to the stream behind the head; longer ones are
+    # graph replays; an explicit eager request is kept at any length
+    assert bench.timing_mode("graph", 1, True) == "eager+head"
+    assert bench.timing_mode("graph", 20, True) == "eager+head"
+    assert bench.timing_mode("graph", bench.EAGER_MAX_STEPS, True) == "eager+head"
+    assert bench.timing_mode("graph", bench.EAGER_MAX_STEPS + 1, True) == "graph"
+    assert bench.timing_mode("graph", 1000, True) == "graph"
+    assert bench.timing_mode("graph", 20, False) == "graph"
+    assert bench.timing_mode("eager", 1000, True) == "eager"
