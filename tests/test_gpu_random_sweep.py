@@ -141,6 +141,35 @@ def test_prefill_random(k):
     assert status in (None, 0)
 
 
+@pytest.mark.parametrize("k", range(12))
+def test_prefill_random_wide(k):
+    """Wider prefill draws (up to 4096 channels and about 12 M elements): the
+    sweep form's grid then holds fewer blocks than there are items, so blocks
+    take several items in turn, and long packed sequences span many items."""
+    rng = np.random.default_rng(99000 + k)
+    D = 8 * int(rng.integers(256, 4096 // 8 + 1))
+    cap = 12_000_000 // D
+    packed = bool(rng.random() < 0.5)
+    if packed:
+        n = int(rng.integers(1, 24))
+        lens = [int(v) for v in rng.integers(0, max(2, 2 * cap // n), size=n)]
+        shape = dict(lens=lens)
+    else:
+        n = int(rng.integers(1, 12))
+        shape = dict(N=n, T=int(rng.integers(cap // (2 * n) + 1, cap // n + 2)))
+    state = [None, "compact", "channel_last"][int(rng.integers(0, 3))]
+    L = int(rng.integers(3, 9))
+    S = n + int(rng.integers(0, 10))
+    routing, n_pad = _routing(rng, n, S) if state is not None else ("none", 0)
+    cfg = dict(L=L, state=state, S=S, routing=routing, n_pad=n_pad,
+               has_init=["none", "all", "mixed"][int(rng.integers(0, 3))], bias=bool(rng.random() < 0.5),
+               act=_act(rng), status=bool(rng.random() < 0.5))
+    _show("prefill-wide", k, D=D, **({"n": n, "tokens": sum(lens)} if packed else shape), **cfg)
+    case = PrefillCase(99500 + k, D, **shape, **cfg)
+    assert case.check() in (None, 0)
+    assert case.kernel.startswith("prefill_sweep_v8<"), case.kernel
+
+
 @pytest.mark.parametrize("k", range(40))
 def test_ring_tokens_random(k):
     rng = np.random.default_rng(99000 + k)
